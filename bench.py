@@ -1,0 +1,209 @@
+"""Benchmark of the verify-attention hot path on one MI355X.
+
+A step is one layer of speculative-verify attention (attn_run + attn_combine through the C ABI)
+over the whole batch, cycling through independent per-layer KV caches so that no layer's cache
+is still in L2/MALL when it is read again (the pages time 16 per-layer working sets under graph
+replay: "DFlash2 concurrent long-context attention", section "Attention-only measurements").
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line: KV read GB/s (whole job), ms per layer, the roofline of the split kernel
+(HBM bytes it must read / its event-timed duration vs 8 TB/s), and the FP64 CPU oracle timed
+on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "verify_b8_ctx128k_gqa6_16layers"
+METRIC = "KV read GB/s (% of 8 TB/s HBM) + attention ms/layer, B8 q8 D256 GQA6 128K ctx"
+COUNTERS = os.path.join(ROOT, "profiles", "split_kernel_e4m3_d256_b8_ctx128k_counters.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("attn_kernels.hip", "attn_internal.h"):
+        with open(os.path.join(ROOT, "verify_attention_e4m3_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(units_per_launch: int):
+    """HBM bytes per split-kernel launch from committed rocprofv3 counters, if they were taken on
+    the current kernel source; otherwise None."""
+    if not os.path.exists(COUNTERS):
+        return None
+    with open(COUNTERS) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return int(rec["hbm_bytes_per_dispatch"])
+
+
+def cpu_baseline(w, case, budget_s: float = 15.0):
+    """The FP64 oracle on (slot, KV head) pairs of layer 0 until about budget_s of CPU work."""
+    import numpy as np
+    import oracle
+    from verify_attention_e4m3_amd import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from _gpu import sample_pairs_numpy
+    pairs_all = [(b, g) for b in range(w.batch) for g in range(w.num_kv_heads)]
+    done, t_total, bytes_total = [], 0.0, 0
+    lens = case["seq_lens"].cpu().tolist()
+    for pair in pairs_all:
+        c = sample_pairs_numpy(case, [pair])
+        t0 = time.perf_counter()
+        oracle.verify_attention(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"],
+                                float(c["k_scale"][0]), float(c["v_scale"][0]), page_size=c["page_size"],
+                                kv_format=c["kv_format"], pairs=[pair])
+        t_total += time.perf_counter() - t0
+        bytes_total += wl.kv_bytes([lens[pair[0]]], 1, w.head_dim, 1 if w.kv_format == "e4m3" else 2)
+        done.append(pair)
+        if t_total >= budget_s:
+            break
+    return {"value": round(bytes_total / t_total / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(done)} of {len(pairs_all)} (slot, KV head) pairs of layer 0 "
+                      f"({bytes_total / 1e9:.3f} GB of KV), FP64 NumPy, {t_total:.1f} s",
+            "ms_per_layer_extrapolated": round(t_total / len(done) * len(pairs_all) * 1e3, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path has no cross-GPU step (each GPU runs its own share "
+              "of requests / KV heads); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from verify_attention_e4m3_amd import attention as A
+    from verify_attention_e4m3_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layers = [wl.workload_case(w, device=dev, layer=i) for i in range(w.layers)]
+    c0 = layers[0]
+    plan = A.Plan(q_len=w.q_len, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                  page_size=w.page_size, max_seq_len=w.max_seq_len, max_pages_per_seq=c0["max_pages_per_seq"],
+                  batch_capacity=w.batch, kv_dtype=w.kv_format, device=dev)
+    ws = torch.empty(plan.workspace_bytes(w.batch) // 4, dtype=torch.float32, device=dev)
+    outs = [torch.empty_like(c["q"]) for c in layers]
+    arglist = [plan.make_args(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"], c["k_scale"],
+                              c["v_scale"], o, ws) for c, o in zip(layers, outs)]
+    elem = 1 if w.kv_format == "e4m3" else 2
+    lens = [int(x) for x in c0["seq_lens"].cpu().tolist()]
+    kv_bytes = wl.kv_bytes(lens, w.num_kv_heads, w.head_dim, elem)
+    token_heads = sum(lens) * w.num_kv_heads
+
+    def step(i):
+        a = arglist[i % w.layers]
+        plan.split(a)
+        plan.combine(a)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K steps, eager, with HIP events around each split-kernel launch on
+    # the stream the kernels are launched on.
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        a = arglist[i % w.layers]
+        ev[i][0].record(stream)
+        plan.split(a)
+        ev[i][1].record(stream)
+        plan.combine(a)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    split_ms = [s.elapsed_time(e) for s, e in ev]
+    split_ms_mean = statistics.fmean(split_ms)
+    achieved = kv_bytes / (split_ms_mean * 1e-3) / 1e9
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+
+    graph = None
+    if not args.no_graph:
+        # The pages' protocol: one graph over the per-layer working sets, 8 replays per sample,
+        # median of 5 samples.
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(w.layers):
+                step(i)
+        g.replay()
+        torch.cuda.synchronize()
+        samples = []
+        for _ in range(5):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(8):
+                g.replay()
+            e.record()
+            torch.cuda.synchronize()
+            samples.append(s.elapsed_time(e) / (8 * w.layers))
+        graph = {"ms_per_layer_median": round(statistics.median(samples), 5),
+                 "ms_per_layer_min": round(min(samples), 5), "ms_per_layer_max": round(max(samples), 5),
+                 "kv_gbs_median": round(kv_bytes / (statistics.median(samples) * 1e-3) / 1e9, 1)}
+
+    # Plain copy probe (read + write of the same byte count as one layer's KV).
+    probe_src = torch.empty(kv_bytes // 2, dtype=torch.uint8, device=dev)
+    probe_dst = torch.empty_like(probe_src)
+    probe_dst.copy_(probe_src)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(10):
+        probe_dst.copy_(probe_src)
+    e.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * probe_src.numel() * 10 / (s.elapsed_time(e) * 1e-3) / 1e9
+    del probe_src, probe_dst
+
+    traffic = measured_traffic(token_heads)
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "q_len": w.q_len,
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "page_size": w.page_size, "kv_format": w.kv_format, "layers": w.layers,
+                   "kv_bytes_per_layer": kv_bytes, "splits_per_row": plan.splits(lens[0])[0]},
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "split_kernel_e4m3_d256", "split_ms_mean": round(split_ms_mean, 5),
+                     "algorithmic_bytes_per_launch": kv_bytes, "units_per_launch": token_heads,
+                     "bytes_per_unit": 2 * w.head_dim * elem},
+        "graph_replay": graph,
+        "copy_probe_gbs": round(copy_gbs, 1),
+        "frac_of_copy_probe": round(value / copy_gbs, 4),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, c0)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,199 @@
+"""C-ABI boundary checks that need no GPU: exports, struct layout, admission, split policy."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+from verify_attention_e4m3_amd import attention as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"ATTN_API\s+[\w\s\*]+?\b(attn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) == 9, names
+    lib = A.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(A.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", A.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert exported == set(names)          # nothing else leaks out of the library
+
+
+def test_struct_layout_matches_the_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "attn.h"
+#define F(T, m) printf(#T "." #m " %zu\n", offsetof(T, m))
+int main(void) {
+  printf("attn_desc %zu\nattn_args %zu\nattn_caps %zu\nattn_plan_info %zu\n",
+         sizeof(attn_desc), sizeof(attn_args), sizeof(attn_caps), sizeof(attn_plan_info));
+  F(attn_desc, k_page_stride); F(attn_desc, v_head_stride); F(attn_desc, sm_scale); F(attn_desc, causal);
+  F(attn_args, num_pages); F(attn_args, workspace_bytes); F(attn_args, out); F(attn_args, batch);
+  F(attn_caps, geometries); F(attn_plan_info, split_bytes);
+  return 0;
+}
+''')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = dict(line.rsplit(" ", 1) for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                                 check=True).stdout.splitlines())
+    assert int(got["attn_desc"]) == ctypes.sizeof(A.attn_desc)
+    assert int(got["attn_args"]) == ctypes.sizeof(A.attn_args)
+    assert int(got["attn_caps"]) == ctypes.sizeof(A.attn_caps)
+    assert int(got["attn_plan_info"]) == ctypes.sizeof(A.attn_plan_info)
+    for key, val in got.items():
+        if "." in key:
+            struct, field = key.split(".")
+            assert getattr(getattr(A, struct), field).offset == int(val), key
+
+
+def test_capabilities():
+    caps = A.capabilities()
+    assert caps["abi_version"] == A.ATTN_ABI_VERSION
+    assert caps["accumulation_bits"] == 32
+    assert caps["page_alignment"] == 16
+    assert caps["max_seq_len"] == 262144
+    assert caps["max_batch"] >= 32
+    assert {"kv_dtype": A.ATTN_KV_E4M3, "head_dim": 256, "max_q_len": 8, "max_rows": 48} in caps["geometries"]
+
+
+def test_status_strings():
+    for s in range(5):
+        assert A.status_string(s)
+    assert A.status_string(99) == "unknown status"
+
+
+BASE = dict(q_len=8, num_q_heads=24, num_kv_heads=4, head_dim=256, page_size=1648, max_seq_len=131072,
+            batch_capacity=8)
+
+
+def plan(**kw):
+    args = dict(BASE)
+    args.update(kw)
+    return A.Plan(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(page_size=1650), A.ATTN_E_INVALID),
+    (dict(page_size=0), A.ATTN_E_INVALID),
+    (dict(num_q_heads=25), A.ATTN_E_INVALID),
+    (dict(max_seq_len=262145), A.ATTN_E_INVALID),
+    (dict(max_seq_len=0), A.ATTN_E_INVALID),
+    (dict(batch_capacity=0), A.ATTN_E_INVALID),
+    (dict(batch_capacity=100000), A.ATTN_E_INVALID),
+    (dict(max_pages_per_seq=10), A.ATTN_E_INVALID),
+    (dict(k_strides=(1648 * 1024, 1024, 252)), A.ATTN_E_INVALID),      # head stride not 8-aligned
+    (dict(v_strides=(0, 1024, 256)), A.ATTN_E_INVALID),
+    (dict(sm_scale=float("nan")), A.ATTN_E_INVALID),
+    (dict(sm_scale=-1.0), A.ATTN_E_INVALID),
+    (dict(sm_scale=float("inf")), A.ATTN_E_INVALID),
+    (dict(abi_version=2), A.ATTN_E_INVALID),
+    (dict(kv_dtype="e5m2"), A.ATTN_E_INVALID),
+    (dict(head_dim=128), A.ATTN_E_UNSUPPORTED),
+    (dict(q_len=9, num_q_heads=4, num_kv_heads=4), A.ATTN_E_UNSUPPORTED),
+    (dict(num_q_heads=28), A.ATTN_E_UNSUPPORTED),                       # G = 7 -> 56 rows > 48
+])
+def test_admission_rejects(kw, status):
+    with pytest.raises(A.AttnError) as e:
+        plan(**kw)
+    assert e.value.status == status
+
+
+@pytest.mark.parametrize("kw", [
+    dict(), dict(page_size=16), dict(page_size=3296, max_seq_len=262144), dict(q_len=1, num_q_heads=4),
+    dict(q_len=8, num_q_heads=4, num_kv_heads=1), dict(causal=False), dict(sm_scale=0.125),
+    dict(k_strides=(1648 * 2056, 2056, 512), v_strides=(1648 * 2056, 2056, 512)),   # interleaved, 8-aligned
+])
+def test_admission_accepts(kw):
+    p = plan(**kw)
+    assert p.info["num_cus"] == 256          # host-only plans assume an MI355X
+    assert p.workspace_bytes(1) * p.batch_capacity == p.workspace_bytes_capacity
+
+
+def test_host_only_plan_cannot_run():
+    p = plan()
+    args = A.attn_args()
+    assert A.lib().attn_run(p.handle, ctypes.byref(args), None) == A.ATTN_E_INVALID
+    assert A.lib().attn_combine(p.handle, ctypes.byref(args), None) == A.ATTN_E_INVALID
+    assert A.lib().attn_run(None, ctypes.byref(args), None) == A.ATTN_E_INVALID
+    assert A.lib().attn_run(p.handle, None, None) == A.ATTN_E_INVALID
+
+
+def test_null_and_bad_arguments():
+    lib = A.lib()
+    assert lib.attn_get_capabilities(None) == A.ATTN_E_INVALID
+    h = ctypes.c_void_p()
+    assert lib.attn_plan(None, -1, ctypes.byref(h), None) == A.ATTN_E_INVALID
+    assert lib.attn_plan_get_info(None, None) == A.ATTN_E_INVALID
+    assert lib.attn_plan_workspace_bytes(None, 1) == 0
+    p = plan()
+    assert lib.attn_plan_workspace_bytes(p.handle, 0) == 0
+    assert lib.attn_plan_workspace_bytes(p.handle, 9) == 0
+    lib.attn_plan_destroy(None)
+
+
+# ---- split policy: a function of the row length and plan constants only ----
+
+LENGTHS = [0, 1, 7, 8, 16, 255, 256, 511, 512, 513, 1024, 3297, 8191, 16384, 32768, 32769, 100000,
+           131072, 200001, 262143, 262144]
+
+
+def test_partitions_cover_each_row_exactly():
+    p = plan(max_seq_len=262144, page_size=3296)
+    info = p.info
+    for L in LENGTHS:
+        S, P = p.splits(L)
+        if L == 0:
+            assert S == 0
+            continue
+        assert P % info["partition_align"] == 0 and P % 32 == 0
+        assert P >= info["partition_min"]
+        assert (S - 1) * P < L <= S * P
+        assert 1 <= S <= info["split_cap"] <= info["grid_splits"] or S <= info["grid_splits"]
+        assert P <= 8192
+
+
+def test_grid_covers_every_length():
+    p = plan(max_seq_len=262144, page_size=3296)
+    gs = p.info["grid_splits"]
+    assert max(p.splits(L)[0] for L in range(0, 262145, 97)) <= gs
+    assert max(p.splits(L)[0] for L in LENGTHS) <= gs
+
+
+def test_split_policy_ignores_batch_and_page_size():
+    a = plan(batch_capacity=1)
+    b = plan(batch_capacity=16, page_size=16)
+    c = plan(batch_capacity=8, page_size=3296, max_seq_len=131072)
+    for L in LENGTHS[:-2]:
+        assert a.splits(L) == b.splits(L) == c.splits(L)
+
+
+def test_long_rows_fill_the_chip():
+    # B8 x 128K at Hkv 4: 8*4*S(131072) single-wave workgroups, one per SIMD of 256 CUs
+    p = plan()
+    S, P = p.splits(131072)
+    assert 8 * 4 * S == 4 * 256
+    assert P == 4096
+
+
+def test_workspace_is_request_major():
+    p = plan()
+    per_slot = p.workspace_bytes(1)
+    assert per_slot == 4 * p.info["grid_splits"] * p.info["split_bytes"]
+    assert p.info["split_bytes"] % 256 == 0
+    assert p.info["split_bytes"] >= (48 * 256 + 96) * 4
+    for b in range(1, 9):
+        assert p.workspace_bytes(b) == b * per_slot

@@ -1,0 +1,248 @@
+"""GPU parity of the HIP path (through the C ABI) against the FP64 oracle, plus the exact
+GPU-vs-GPU invariants: batched == single request, page size / permutation invariance,
+replay == eager, run-to-run determinism. Every test here needs an MI355X."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _gpu import compare, note, oracle_pairs, plan_for, run_gpu, run_oracle, to_gpu
+from verify_attention_e4m3_amd import attention as A
+from verify_attention_e4m3_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(**kw):
+    return to_gpu(wl.make_case(**kw))
+
+
+def test_e4m3_bytes_decode_exactly():
+    # L == q_len: verify token 0 sees only key 0, whose V row holds all 254 finite E4M3
+    # byte values; softmax of one key is 1, so the output is exactly those values in FP16.
+    note("e4m3 all bytes, B1 L8 Hq6 Hkv1 page16")
+    c = _case(batch=1, seq_lens=[8], q_len=8, num_q_heads=6, num_kv_heads=1, head_dim=256, page_size=16, seed=101)
+    vals = np.arange(256, dtype=np.uint8)
+    vals[[0x7F, 0xFF]] = 0
+    page = int(c["block_table"][0, 0])
+    c["v_cache"][page, 0, 0, :] = torch.from_numpy(vals).cuda()
+    out = run_gpu(c)
+    want = torch.from_numpy(oracle.decode_table()[vals].astype(np.float16)).cuda()
+    for h in range(6):
+        assert torch.equal(out[0, 0, h].view(torch.int16), want.view(torch.int16)), h
+
+
+SMALL = [
+    dict(batch=1, seq_lens=[1], q_len=8, num_q_heads=6, num_kv_heads=1, page_size=16),
+    dict(batch=1, seq_lens=[8], q_len=8, num_q_heads=6, num_kv_heads=1, page_size=16),
+    dict(batch=2, seq_lens=[5, 33], q_len=8, num_q_heads=6, num_kv_heads=1, page_size=16),
+    dict(batch=3, seq_lens=[100, 17, 64], q_len=8, num_q_heads=12, num_kv_heads=2, page_size=32),
+    dict(batch=2, seq_lens=[513, 1025], q_len=8, num_q_heads=24, num_kv_heads=4, page_size=48),
+    dict(batch=4, seq_lens=[0, 700, 1, 2000], q_len=8, num_q_heads=24, num_kv_heads=4, page_size=1648),
+    dict(batch=2, seq_lens=[1000, 31], q_len=4, num_q_heads=16, num_kv_heads=4, page_size=16),
+    dict(batch=2, seq_lens=[40, 600], q_len=1, num_q_heads=6, num_kv_heads=1, page_size=16),
+    dict(batch=1, seq_lens=[5000], q_len=8, num_q_heads=32, num_kv_heads=8, page_size=64),
+    dict(batch=2, seq_lens=[4097, 9000], q_len=8, num_q_heads=6, num_kv_heads=1, page_size=3296, kv_std=0.25,
+         kv_scale=3.0),
+]
+
+
+@pytest.mark.parametrize("kw", SMALL, ids=lambda kw: f"B{kw['batch']}-L{max(kw['seq_lens'])}-q{kw['q_len']}-"
+                                                      f"H{kw['num_q_heads']}/{kw['num_kv_heads']}-p{kw['page_size']}")
+def test_parity_small(kw):
+    note(f"parity small {kw}")
+    c = _case(head_dim=256, seed=sum(kw["seq_lens"]) + kw["page_size"], **kw)
+    stats = compare(run_gpu(c), run_oracle(c))
+    assert stats["rows"] > 0
+
+
+def test_parity_non_causal_and_custom_scale():
+    note("parity non-causal, sm_scale 0.05")
+    c = _case(batch=2, seq_lens=[77, 1500], q_len=8, num_q_heads=6, num_kv_heads=1, head_dim=256, page_size=16,
+              seed=7, kv_scale=0.5)
+    out = run_gpu(c, causal=False, sm_scale=0.05)
+    compare(out, run_oracle(c, causal=False, sm_scale=0.05))
+
+
+def test_parity_distinct_k_and_v_scales():
+    note("parity k_scale 0.25, v_scale 4")
+    c = _case(batch=2, seq_lens=[333, 2048], q_len=8, num_q_heads=12, num_kv_heads=2, head_dim=256, page_size=32,
+              seed=8)
+    c["k_scale"].fill_(0.25)
+    c["v_scale"].fill_(4.0)
+    compare(run_gpu(c), run_oracle(c))
+
+
+@pytest.mark.parametrize("name", ["verify_b1_ctx3297_hq6_hkv1", "verify_b4_ctx32k_gqa6"])
+def test_parity_workload_full(name):
+    note(f"parity full workload {name}")
+    w = wl.WORKLOADS[name]
+    c = to_gpu(wl.workload_case(w))
+    stats = compare(run_gpu(c), run_oracle(c))
+    assert stats["rows"] == w.batch * w.q_len * w.num_q_heads
+
+
+def test_batched_equals_single_bitwise():
+    note("batched vs single, B5 mixed lengths")
+    c = _case(batch=5, seq_lens=[3297, 0, 40000, 8, 131], q_len=8, num_q_heads=24, num_kv_heads=4, head_dim=256,
+              page_size=1648, seed=9, max_seq_len=65536)
+    batched = run_gpu(c, batch_capacity=16)
+    for b in range(5):
+        one = {k: (v[b:b + 1] if k in ("q", "block_table", "seq_lens") else v) for k, v in c.items()}
+        single = run_gpu(one, batch_capacity=1)
+        assert torch.equal(single[0].view(torch.int16), batched[b].view(torch.int16)), b
+
+
+def _repaged(c, page_size, seed):
+    """The same logical tokens laid out with another page size and a shuffled page order."""
+    ps0 = c["page_size"]
+    B = c["q"].shape[0]
+    lens = c["seq_lens"].cpu().tolist()
+    Lmax = max(lens)
+    npg = -(-Lmax // page_size)
+    rng = np.random.default_rng(seed)
+    pool = B * npg + 5
+    perm = torch.from_numpy(rng.permutation(pool)).cuda()
+    Hkv, D = c["k_cache"].shape[2], c["k_cache"].shape[3]
+    k2 = torch.zeros((pool, page_size, Hkv, D), dtype=c["k_cache"].dtype, device="cuda")
+    v2 = torch.zeros_like(k2)
+    table = torch.full((B, npg), -1, dtype=torch.int32, device="cuda")
+    for b in range(B):
+        L = lens[b]
+        j = torch.arange(L, device="cuda")
+        src_pages = c["block_table"][b].long()[j // ps0]
+        tok_k = c["k_cache"][src_pages, j % ps0]
+        tok_v = c["v_cache"][src_pages, j % ps0]
+        dst_pages = perm[b * npg: b * npg + npg]
+        table[b, :] = dst_pages.int()
+        k2[dst_pages[j // page_size], j % page_size] = tok_k
+        v2[dst_pages[j // page_size], j % page_size] = tok_v
+    out = dict(c)
+    out.update(k_cache=k2, v_cache=v2, block_table=table, page_size=page_size)
+    return out
+
+
+def test_page_size_and_permutation_invariance_bitwise():
+    note("page size / permutation invariance")
+    c = _case(batch=3, seq_lens=[9000, 1234, 17], q_len=8, num_q_heads=12, num_kv_heads=2, head_dim=256,
+              page_size=1648, seed=10, max_seq_len=9000)
+    base = run_gpu(c)
+    for ps, seed in [(16, 1), (1648, 2), (3296, 3), (48, 4)]:
+        other = run_gpu(_repaged(c, ps, seed), max_seq_len=9000)
+        assert torch.equal(other.view(torch.int16), base.view(torch.int16)), ps
+
+
+def test_zero_length_and_padded_slots():
+    note("zero-length rows and padded slots")
+    c = _case(batch=6, seq_lens=[0, 300, 0, 1700, 0, 0], q_len=8, num_q_heads=24, num_kv_heads=4, head_dim=256,
+              page_size=16, seed=11, padded_slots=[4, 5])
+    out = run_gpu(c)
+    compare(out, run_oracle(c))
+    for b in (0, 2, 4, 5):
+        assert (out[b].view(torch.int16) == 0).all(), b          # exactly +0
+    # all-zero batch
+    c["seq_lens"].zero_()
+    out = run_gpu(c)
+    assert (out.view(torch.int16) == 0).all()
+
+
+def test_interleaved_eight_byte_aligned_strides():
+    note("interleaved K/V, 8-byte-only aligned strides")
+    B, L, Hkv, Hq, D, ps = 2, 700, 2, 12, 256, 32
+    c = wl.make_case(batch=B, seq_lens=[L, 333], q_len=8, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                     page_size=ps, seed=12)
+    pool = c["k_cache"].shape[0]
+    rec = 2 * D + 8                 # per (token, head): K bytes, V bytes, 8 pad bytes -> 520, not 16-aligned
+    tok = Hkv * rec
+    page = ps * tok + 8
+    buf = torch.zeros(pool * page + 64, dtype=torch.uint8)
+    base = 8                          # base address 8 mod 16
+    kview = torch.as_strided(buf, (pool, ps, Hkv, D), (page, tok, rec, 1), base)
+    vview = torch.as_strided(buf, (pool, ps, Hkv, D), (page, tok, rec, 1), base + D)
+    kview.copy_(c["k_cache"])
+    vview.copy_(c["v_cache"])
+    g = to_gpu(c)
+    gbuf = buf.cuda()
+    plan = plan_for(g, k_strides=(page, tok, rec), v_strides=(page, tok, rec))
+    out = torch.empty_like(g["q"])
+    ws = A.default_bank().get(plan, B)
+    args = plan.make_args(g["q"], gbuf.data_ptr() + base, gbuf.data_ptr() + base + D, g["block_table"],
+                          g["seq_lens"], g["k_scale"], g["v_scale"], out, ws, num_pages=pool)
+    plan.split(args)
+    plan.combine(args)
+    torch.cuda.synchronize()
+    compare(out, run_oracle(c))
+
+
+def test_repeatable_bitwise():
+    note("run-to-run determinism")
+    c = _case(batch=2, seq_lens=[20000, 5000], q_len=8, num_q_heads=24, num_kv_heads=4, head_dim=256,
+              page_size=1648, seed=13)
+    a = run_gpu(c)
+    b = run_gpu(c)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_reference_slack_overflow_recompute():
+    # The first tile's scores are 0; later spikes score 16 (23 log2 units) above that, beyond
+    # the slack of a row's first-tile reference, so each split is recomputed with exact maxima.
+    note("reference overflow -> exact recompute")
+    c = _case(batch=1, seq_lens=[900], q_len=8, num_q_heads=6, num_kv_heads=1, head_dim=256, page_size=16,
+              seed=14)
+    c["q"].fill_(1.0)
+    table = c["block_table"][0].long()
+    kc = c["k_cache"]
+    one = 0x38                        # E4M3 1.0
+    for j in range(0, 64):            # first two tiles: keys 0 -> score 0
+        kc[table[j // 16], j % 16, 0, :] = 0
+    for j in range(64, 900):          # later keys: mostly 0, a few spikes of score 16 (23 log2 units)
+        kc[table[j // 16], j % 16, 0, :] = one if j % 97 == 0 else 0
+    out = run_gpu(c)
+    compare(out, run_oracle(c))
+    # a milder rise (< the slack) takes the single-pass path and must also match
+    for j in range(64, 900):
+        kc[table[j // 16], j % 16, 0, :] = 0x2C if j % 97 == 0 else 0     # 0.375 -> score 6 (8.7 log2 units)
+    compare(run_gpu(c), run_oracle(c))
+
+
+def _graph(plan, case, out, ws):
+    args = plan.make_args(case["q"], case["k_cache"], case["v_cache"], case["block_table"], case["seq_lens"],
+                          case["k_scale"], case["v_scale"], out, ws)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        plan.split(args, s)           # warm up on the capture stream
+        plan.combine(args, s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        plan.split(args)
+        plan.combine(args)
+    return g, args
+
+
+def test_graph_replay_with_changed_inputs_matches_eager():
+    note("graph replay with changed Q, lengths, zero rows, scales")
+    B, Lmax = 4, 6000
+    c = _case(batch=B, seq_lens=[Lmax] * B, q_len=8, num_q_heads=24, num_kv_heads=4, head_dim=256, page_size=1648,
+              seed=15, max_seq_len=Lmax)
+    plan = plan_for(c)
+    out = torch.empty_like(c["q"])
+    ws = torch.empty(plan.workspace_bytes(B) // 4, dtype=torch.float32, device="cuda")
+    g, _ = _graph(plan, c, out, ws)
+    rng = np.random.default_rng(16)
+    for rep, lens in enumerate([[6000, 3297, 0, 1], [0, 0, 0, 0], [17, 5999, 4000, 0], [6000, 6000, 6000, 6000]]):
+        c["q"].copy_(torch.randn(c["q"].shape, generator=torch.Generator("cuda").manual_seed(100 + rep),
+                                 device="cuda").half())
+        c["seq_lens"].copy_(torch.tensor(lens, dtype=torch.int32))
+        c["k_scale"].fill_(float(rng.choice([0.5, 1.0, 2.0])))
+        c["v_scale"].fill_(float(rng.choice([0.5, 1.0, 3.0])))
+        g.replay()
+        torch.cuda.synchronize()
+        replayed = out.clone()
+        eager = run_gpu(c)
+        assert torch.equal(replayed.view(torch.int16), eager.view(torch.int16)), rep
+        compare(replayed, run_oracle(c))

@@ -1,0 +1,77 @@
+"""GPU parity at the full sizes of the long-context workloads, in the launch configuration the
+benchmark times: B8 x 131072 (sampled (slot, KV head) pairs checked against the oracle) and
+B16 mixed lengths up to 262144 with page 3296, captured once in a graph and replayed with
+fresh queries, lengths and zero rows."""
+import numpy as np
+import pytest
+import torch
+
+from _gpu import compare, note, oracle_pairs, plan_for
+from verify_attention_e4m3_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def test_b8_ctx128k_sampled_pairs():
+    w = wl.WORKLOADS["verify_b8_ctx128k_gqa6_16layers"]
+    note(f"{w.name} layer 0, sampled pairs")
+    c = wl.workload_case(w, device="cuda", layer=0)
+    plan = plan_for(c)
+    out = plan.run(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"], c["k_scale"], c["v_scale"])
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (7, 3), (3, 1)]
+    stats = compare(out, oracle_pairs(c, pairs))
+    assert stats["rows"] == len(pairs) * w.q_len * w.group
+    assert torch.isfinite(out.float()).all()
+
+
+def test_b16_mixed_graph_replays():
+    w = wl.WORKLOADS["verify_b16_mixed_ctx256k_page3296"]
+    note(f"{w.name} graph capture at B16/262144, replays with seeds 40..42")
+    B = w.batch
+    padded = list(range(B - 3, B))
+    alloc = [w.max_seq_len] * (B - 3) + [0] * 3
+    c = wl.make_case(batch=B, seq_lens=wl.mixed_lengths(B, w.seed), q_len=w.q_len, num_q_heads=w.num_q_heads,
+                     num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, page_size=w.page_size, seed=w.seed,
+                     device="cuda", max_seq_len=w.max_seq_len, alloc_lens=alloc, padded_slots=padded)
+    plan = plan_for(c)
+    out = torch.empty_like(c["q"])
+    ws = torch.empty(plan.workspace_bytes(B) // 4, dtype=torch.float32, device="cuda")
+    args = plan.make_args(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"], c["k_scale"],
+                          c["v_scale"], out, ws)
+    plan.split(args)
+    plan.combine(args)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan.split(args)
+        plan.combine(args)
+    for seed in (40, 41, 42):
+        lens = wl.mixed_lengths(B, seed)
+        note(f"replay seed {seed} lengths {lens}")
+        c["seq_lens"].copy_(torch.tensor(lens, dtype=torch.int32))
+        q = torch.randn(c["q"].shape, generator=torch.Generator("cuda").manual_seed(seed), device="cuda").half()
+        q[padded] = float("nan")
+        c["q"].copy_(q)
+        for rep in range(2):
+            g.replay()
+            torch.cuda.synchronize()
+            if rep == 0:
+                first = out.clone()
+        assert torch.equal(first.view(torch.int16), out.view(torch.int16))
+        live = [b for b in range(B) if lens[b] > 0]
+        longest = max(live, key=lambda b: lens[b])
+        shortest = min(live, key=lambda b: lens[b])
+        pairs = [(longest, 0), (longest, 3), (shortest, 1), (shortest, 2)]
+        compare(out, oracle_pairs(c, pairs))
+        for b in range(B):
+            if lens[b] == 0:
+                assert (out[b].view(torch.int16) == 0).all(), b
+        # eager execution of the same inputs gives the replayed bits
+        eager = torch.empty_like(out)
+        args_e = plan.make_args(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"], c["k_scale"],
+                                c["v_scale"], eager, ws)
+        plan.split(args_e)
+        plan.combine(args_e)
+        torch.cuda.synchronize()
+        assert torch.equal(eager.view(torch.int16), out.view(torch.int16))

@@ -1,0 +1,102 @@
+// attn_internal.h - plan layout, split policy and kernel parameters shared by the host plan
+// code (attn_plan.cpp) and the kernels (attn_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "attn.h"
+
+#if defined(__HIP__)
+#define ATTN_HD static inline __host__ __device__
+#else
+#define ATTN_HD static inline
+#endif
+
+namespace attn {
+
+// Row-tile geometry of the E4M3 D=256 kernel: 3 tiles of 16 packed rows (q_len * G <= 48).
+constexpr int kRowTiles = 3;
+constexpr int kRowsAlloc = 16 * kRowTiles;
+constexpr int kTileTokens = 32;        // tokens per inner iteration of one wave
+constexpr int kMaxBatch = 256;
+constexpr int kMaxSeqLen = 262144;
+constexpr int kPageAlign = 16;
+constexpr int kStrideAlign = 8;
+constexpr int kWorkspaceAlign = 256;
+
+// Split policy: a row of length L is cut into S(L) token partitions of P(L) tokens (the last
+// one shorter). P depends only on L and on plan constants, never on the batch or other rows,
+// so a request's partial sums - and therefore its output bits - are the same whether it runs
+// alone or batched (the bitwise batched == single requirement of the DFlash2 long-batch note,
+// "Operator validation"). P is a multiple of the kernel tile so tiles never straddle splits.
+struct SplitPolicy {
+    int32_t split_cap;     // at most this many splits per (slot, KV head)
+    int32_t part_min;      // shortest partition
+    int32_t part_align;    // partitions are multiples of this (a multiple of kTileTokens)
+};
+
+ATTN_HD int32_t partition_len(int32_t L, SplitPolicy p) {
+    int32_t want = (L + p.split_cap - 1) / p.split_cap;
+    want = ((want + p.part_align - 1) / p.part_align) * p.part_align;
+    return want < p.part_min ? p.part_min : want;
+}
+
+ATTN_HD int32_t num_splits(int32_t L, SplitPolicy p) {
+    if (L <= 0) return 0;
+    const int32_t P = partition_len(L, p);
+    return (L + P - 1) / P;
+}
+
+// Kernel parameters, passed by value (a captured hipGraph keeps a copy; nothing points at
+// host memory).
+struct RunParams {
+    const uint16_t* q;            // FP16 bits [batch][q_len][Hq][D]
+    const uint8_t* k;             // cache bases (byte addressed)
+    const uint8_t* v;
+    const int32_t* block_table;   // [batch][bt_stride]
+    const int32_t* seq_lens;      // [batch]
+    const float* k_scale;
+    const float* v_scale;
+    float* ws;                    // split panels
+    uint16_t* out;                // FP16 bits [batch][q_len][Hq][D]
+    int64_t k_page_stride, k_token_stride, k_head_stride;
+    int64_t v_page_stride, v_token_stride, v_head_stride;
+    int64_t num_pages;
+    int32_t bt_stride;
+    int32_t page_size;
+    uint64_t page_magic;          // ceil(2^40 / page_size): j / page_size = (j * page_magic) >> 40
+    int32_t max_seq_len;
+    int32_t q_len;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t group;                // Hq / Hkv
+    int32_t rows;                 // q_len * group
+    int32_t grid_splits;          // splits per (slot, KV head) in the grid
+    int32_t causal;
+    int32_t split_floats;         // floats per split panel
+    int32_t batch;
+    float sm_scale;
+    SplitPolicy policy;
+};
+
+}  // namespace attn
+
+struct attn_plan_s {
+    attn_desc desc;
+    int device;                    // HIP ordinal, or ATTN_DEVICE_HOST_ONLY
+    int num_cus;
+    attn::SplitPolicy policy;
+    int32_t grid_splits;
+    int32_t rows;
+    float sm_scale;
+    size_t split_floats;
+    size_t split_bytes;
+    size_t workspace_bytes;        // for desc.batch_capacity slots
+};
+
+// Launchers implemented in attn_kernels.hip (host side of the HIP translation unit).
+attn_status attn_launch_split(const attn_plan_s* plan, const attn::RunParams& p, void* stream);
+attn_status attn_launch_combine(const attn_plan_s* plan, const attn::RunParams& p, void* stream);
+attn_status attn_device_cus(int device, int* num_cus);
+attn_status attn_stream_device(void* stream, int* device);
