@@ -48,6 +48,29 @@ def measured_traffic(units_per_launch: int):
     return int(rec["hbm_bytes_per_dispatch"])
 
 
+def stream_read_probe(torch, dev, nbytes: int, reps: int = 10) -> float:
+    """GB/s of a plain streaming-read kernel (libattn_probe.so) over nbytes of device memory."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "verify_attention_e4m3_amd", "libattn_probe.so"))
+    lib.attn_probe_stream_read.restype = ctypes.c_int
+    lib.attn_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                           ctypes.c_void_p]
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    grid = 2048
+    sink = torch.empty(grid * 4, dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    if lib.attn_probe_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), grid, stream) != 0:
+        raise RuntimeError("stream probe launch failed")
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        lib.attn_probe_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), grid, stream)
+    e.record()
+    torch.cuda.synchronize()
+    return nbytes * reps / (s.elapsed_time(e) * 1e-3) / 1e9
+
+
 def cpu_baseline(w, case, budget_s: float = 15.0):
     """The FP64 oracle on (slot, KV head) pairs of layer 0 until about budget_s of CPU work."""
     import numpy as np
@@ -167,7 +190,8 @@ def main():
                  "ms_per_layer_min": round(min(samples), 5), "ms_per_layer_max": round(max(samples), 5),
                  "kv_gbs_median": round(kv_bytes / (statistics.median(samples) * 1e-3) / 1e9, 1)}
 
-    # Plain copy probe (read + write of the same byte count as one layer's KV).
+    # Plain copy probe (read + write of the same byte count as one layer's KV); its rocprofv3
+    # FETCH_SIZE / WRITE_SIZE readings calibrate those counters against a known byte count.
     probe_src = torch.empty(kv_bytes // 2, dtype=torch.uint8, device=dev)
     probe_dst = torch.empty_like(probe_src)
     probe_dst.copy_(probe_src)
@@ -180,7 +204,7 @@ def main():
     torch.cuda.synchronize()
     copy_gbs = 2 * probe_src.numel() * 10 / (s.elapsed_time(e) * 1e-3) / 1e9
     del probe_src, probe_dst
-
+    read_gbs = stream_read_probe(torch, dev, kv_bytes)
     traffic = measured_traffic(token_heads)
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -198,7 +222,9 @@ def main():
                      "bytes_per_unit": 2 * w.head_dim * elem},
         "graph_replay": graph,
         "copy_probe_gbs": round(copy_gbs, 1),
-        "frac_of_copy_probe": round(value / copy_gbs, 4),
+        "read_probe_gbs": round(read_gbs, 1),
+        "split_frac_of_read_probe": round(achieved / read_gbs, 4),
+        "split_ms_p10_p50_p90": [round(x, 5) for x in statistics.quantiles(split_ms, n=10)[0::4]],
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, c0)

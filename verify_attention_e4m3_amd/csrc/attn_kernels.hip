@@ -55,6 +55,14 @@ __device__ __forceinline__ half8 e4m3x8(uint32_t lo, uint32_t hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max of three floats in one v_max3_f32. fmaxf would first quiet each operand (IEEE mode);
+// the scores here are finite or -inf, so no quieting is needed.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 __device__ __forceinline__ int32_t clamp_len(int32_t L, int32_t max_len) {
     return L < 0 ? 0 : (L > max_len ? max_len : L);
 }
@@ -76,51 +84,68 @@ __device__ __forceinline__ void locate(int32_t j, const RunParams& p, int32_t& p
     slot = j - page_idx * p.page_size;
 }
 
-// Per-lane global addresses of one tile (j0 <= last, the split's last token). Granule A
-// covers j0..j0+15 and granule B j0+16..j0+31; tokens past `last` (and all of B when it starts
-// past it) re-read token `last`, whose page exists; they are masked in the softmax.
-struct TileAddr {
-    const uint8_t* kA;   // lane's K row in granule A (+16*qd)
-    const uint8_t* kB;
-    const uint8_t* vA;   // V row base of granule A (slot offset added per lane)
-    const uint8_t* vB;
-    int32_t tA, tB;      // V: token index of slot 0 within A / B before clamping, see v_row()
-    int32_t j0, gsB, last;
+// Per-lane byte offsets of a full tile within its two granules, fixed for the whole split.
+// Every load instruction reads whole 256-byte token rows, 16 lanes per row, 4 rows per
+// instruction, so each one is eight 128-byte lines.
+// K: instruction i (0..7) covers tokens 16*(i/4) + 4*(i%4) + (lane/16) of the tile; lane l
+//    fetches 16-byte chunk (l%16) ^ (token%16) of its row into LDS slot l%16. The XOR swizzle
+//    lets the MFMA-order reads of the consumer (16 lanes = 16 tokens, same chunk) hit 16
+//    different LDS bank groups.
+// V: slot e of lane (n, qd) is token 4*qd + (e&3) of granule e>>2, dims 16*n + 0..15 - the
+//    lane that loads a chunk is the lane that consumes it.
+struct LaneOffs {
+    uint32_t k[4];
+    uint32_t v[4];
 };
 
-__device__ __forceinline__ TileAddr tile_addr(int32_t j0, int32_t last, const int32_t* pages, int32_t pg0,
-                                              const uint8_t* kbase, const uint8_t* vbase, const RunParams& p, int n,
-                                              int qd) {
-    TileAddr a;
-    a.j0 = j0;
-    a.last = last;
-    a.gsB = min(j0 + 16, last & ~15);
+__device__ __forceinline__ LaneOffs lane_offsets(const RunParams& p, int lane, int n, int qd) {
+    LaneOffs o;
+    const int tr = lane >> 4, slot = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tok = 4 * i + tr;                    // token within the granule
+        o.k[i] = (uint32_t)(tok * p.k_token_stride + 16 * (slot ^ tok));
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o.v[e] = (uint32_t)((4 * qd + e) * p.v_token_stride + 16 * n);
+    return o;
+}
+
+// Uniform byte addresses of the first tokens of a tile's two granules (A at j0, B at gsB) in
+// the K and V caches of this KV head.
+struct Granules {
+    const uint8_t* kA;
+    const uint8_t* kB;
+    const uint8_t* vA;
+    const uint8_t* vB;
+    int32_t j0, gsB;
+};
+
+__device__ __forceinline__ Granules granules(int32_t j0, int32_t last, const int32_t* pages, int32_t pg0,
+                                             const uint8_t* kbase, const uint8_t* vbase, const RunParams& p) {
+    Granules gr;
+    gr.j0 = j0;
+    gr.gsB = min(j0 + 16, last & ~15);
     int32_t ia, sa, ib, sb;
     locate(j0, p, ia, sa);
-    locate(a.gsB, p, ib, sb);
+    locate(gr.gsB, p, ib, sb);
     const int64_t pageA = __builtin_amdgcn_readfirstlane(pages[ia - pg0]);
     const int64_t pageB = __builtin_amdgcn_readfirstlane(pages[ib - pg0]);
-    const uint8_t* kA = kbase + pageA * p.k_page_stride + (int64_t)sa * p.k_token_stride;
-    const uint8_t* kB = kbase + pageB * p.k_page_stride + (int64_t)sb * p.k_token_stride;
-    a.vA = vbase + pageA * p.v_page_stride + (int64_t)sa * p.v_token_stride + 16 * n;
-    a.vB = vbase + pageB * p.v_page_stride + (int64_t)sb * p.v_token_stride + 16 * n;
-    a.kA = kA + (int64_t)(min(j0 + n, last) - j0) * p.k_token_stride + 16 * qd;
-    a.kB = kB + (int64_t)(min(j0 + 16 + n, last) - a.gsB) * p.k_token_stride + 16 * qd;
-    return a;
+    gr.kA = kbase + pageA * p.k_page_stride + (int64_t)sa * p.k_token_stride;
+    gr.kB = kbase + pageB * p.k_page_stride + (int64_t)sb * p.k_token_stride;
+    gr.vA = vbase + pageA * p.v_page_stride + (int64_t)sa * p.v_token_stride;
+    gr.vB = vbase + pageB * p.v_page_stride + (int64_t)sb * p.v_token_stride;
+    return gr;
 }
 
-__device__ __forceinline__ const uint8_t* v_row(const TileAddr& a, int e, int qd, int64_t tok_stride) {
-    const int rel = 4 * qd + (e & 3);
-    return e < 4 ? a.vA + (int64_t)(min(a.j0 + rel, a.last) - a.j0) * tok_stride
-                 : a.vB + (int64_t)(min(a.j0 + 16 + rel, a.last) - a.gsB) * tok_stride;
-}
-
-// Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at lds + 16*l. Issued as
-// inline asm so that the compiler's wait-count pass, which cannot tell the two ring stages
-// apart and would wait for every LDS load before any LDS read, leaves the waiting to the
-// explicit vmcnt waits of the tile loop.
-__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gaddr) : "memory", "m0");
+// Direct global -> LDS load of 16 bytes per lane from base + voff: lane l's bytes land at
+// lds + 16*l. Issued as inline asm so that the compiler's wait-count pass, which cannot tell
+// the two ring stages apart and would wait for every LDS load before any LDS read, leaves the
+// waiting to the explicit vmcnt waits of the tile loop. The KV cache is read exactly once, so
+// the loads carry the non-temporal (streaming) hint.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(lds), "v"(voff), "s"(base)
+                 : "memory", "m0");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -131,17 +156,48 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 constexpr int kStageRows = 16;
 constexpr int kStageBytes = kStageRows * 64 * 16;
 
-__device__ __forceinline__ void issue_k(const TileAddr& a, uint32_t stage) {
+// A tile whose 32 tokens all precede `last` uses the split's fixed lane offsets; the tail tile
+// clamps each lane's token to `last` (whose page exists; the extra tokens are masked).
+__device__ __forceinline__ void issue_k(const Granules& gr, int32_t last, const LaneOffs& lo, uint32_t stage,
+                                        const RunParams& p, int lane) {
+    if (gr.j0 + kTileTokens - 1 <= last) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        dma16(a.kA + 64 * i, stage + i * 1024);
-        dma16(a.kB + 64 * i, stage + (4 + i) * 1024);
+        for (int i = 0; i < 4; ++i) {
+            dma16(gr.kA, lo.k[i], stage + i * 1024);
+            dma16(gr.kB, lo.k[i], stage + (4 + i) * 1024);
+        }
+    } else {
+        const int tr = lane >> 4, slot = lane & 15;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = 4 * i + tr;
+            const uint32_t oa = (uint32_t)((min(gr.j0 + tok, last) - gr.j0) * p.k_token_stride + 16 * (slot ^ tok));
+            const uint32_t ob =
+                (uint32_t)((min(gr.j0 + 16 + tok, last) - gr.gsB) * p.k_token_stride + 16 * (slot ^ tok));
+            dma16(gr.kA, oa, stage + i * 1024);
+            dma16(gr.kB, ob, stage + (4 + i) * 1024);
+        }
     }
 }
 
-__device__ __forceinline__ void issue_v(const TileAddr& a, uint32_t stage, int qd, int64_t tok_stride) {
+__device__ __forceinline__ void issue_v(const Granules& gr, int32_t last, const LaneOffs& lo, uint32_t stage,
+                                        const RunParams& p, int n, int qd) {
+    if (gr.j0 + kTileTokens - 1 <= last) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dma16(v_row(a, e, qd, tok_stride), stage + (8 + e) * 1024);
+        for (int e = 0; e < 4; ++e) {
+            dma16(gr.vA, lo.v[e], stage + (8 + e) * 1024);
+            dma16(gr.vB, lo.v[e], stage + (12 + e) * 1024);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int rel = 4 * qd + e;
+            const uint32_t oa = (uint32_t)((min(gr.j0 + rel, last) - gr.j0) * p.v_token_stride + 16 * n);
+            const uint32_t ob = (uint32_t)((min(gr.j0 + 16 + rel, last) - gr.gsB) * p.v_token_stride + 16 * n);
+            dma16(gr.vA, oa, stage + (8 + e) * 1024);
+            dma16(gr.vB, ob, stage + (12 + e) * 1024);
+        }
+    }
 }
 
 __device__ __forceinline__ void vm_wait_tile() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
@@ -168,32 +224,40 @@ __device__ __forceinline__ void qk_tile(const TileK& t, float4v (&sacc)[2][kRowT
     }
 }
 
-// Softmax step of one tile: scaled, masked scores (lane holds row n's tokens
-// j0 + 16*tt + 4*qd + i), exponentials against the row references, P^T in FP16. Returns true
-// (uniformly) when a row's tile max exceeds its reference by more than kRefSlack; the
-// references are then raised and nothing was accumulated.
+// Softmax step of one tile: masked raw scores (lane holds row n's tokens j0 + 16*tt + 4*qd + i),
+// exponentials exp2(c*x - m) against the row references (c > 0, log2 units), P^T in FP16.
+// Returns true (uniformly) when a row's tile max exceeds its reference by more than kRefSlack;
+// the references are then raised and nothing was accumulated.
 __device__ __forceinline__ bool softmax_tile(const float4v (&sacc)[2][kRowTiles], int32_t j0, int32_t mask_from,
                                              const int32_t (&lim)[kRowTiles], float c, float (&m_ref)[kRowTiles],
                                              float (&l_run)[kRowTiles], half8 (&pop)[kRowTiles], int qd) {
-    const bool need_mask = j0 + kTileTokens > mask_from;
     float x[kRowTiles][8];
+#pragma unroll
+    for (int rt = 0; rt < kRowTiles; ++rt)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[rt][tt * 4 + i] = sacc[tt][rt][i];
+    if (j0 + kTileTokens > mask_from) {      // only tiles at the causal tail or the row end
+#pragma unroll
+        for (int rt = 0; rt < kRowTiles; ++rt)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    x[rt][tt * 4 + i] = (j0 + 16 * tt + 4 * qd + i) < lim[rt] ? x[rt][tt * 4 + i] : -INFINITY;
+    }
     float mx[kRowTiles];
     bool over = false;
 #pragma unroll
     for (int rt = 0; rt < kRowTiles; ++rt) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float v = sacc[tt][rt][i] * c;
-                if (need_mask) v = (j0 + 16 * tt + 4 * qd + i) < lim[rt] ? v : -INFINITY;
-                x[rt][tt * 4 + i] = v;
-            }
-        float m = x[rt][0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) m = fmaxf(m, x[rt][e]);
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
+        float m = max3f(max3f(x[rt][0], x[rt][1], x[rt][2]), max3f(x[rt][3], x[rt][4], x[rt][5]),
+                        max3f(x[rt][6], x[rt][7], x[rt][7]));
+        const float m16 = __shfl_xor(m, 16);
+        m = max3f(m, m16, m16);
+        const float m32 = __shfl_xor(m, 32);
+        m = max3f(m, m32, m32);
+        m *= c;                                      // c > 0: max commutes with the scale
         mx[rt] = m;
         over |= m > m_ref[rt] + kRefSlack && m_ref[rt] != -INFINITY;
     }
@@ -205,15 +269,13 @@ __device__ __forceinline__ bool softmax_tile(const float4v (&sacc)[2][kRowTiles]
 #pragma unroll
     for (int rt = 0; rt < kRowTiles; ++rt) {
         if (m_ref[rt] == -INFINITY) m_ref[rt] = mx[rt];        // first tile with a visible key
-        const float m_use = m_ref[rt] == -INFINITY ? 0.0f : m_ref[rt];
-        float sum = 0.0f;
+        const float neg_m = m_ref[rt] == -INFINITY ? 0.0f : -m_ref[rt];
+        float pe[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float pe = fast_exp2(x[rt][e] - m_use);
-            sum += pe;
-            pop[rt][e] = (_Float16)pe;
-        }
-        l_run[rt] += sum;      // lane-partial; reduced across the quarters at the end
+        for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(__builtin_fmaf(x[rt][e], c, neg_m));
+        l_run[rt] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pop[rt][e] = (_Float16)pe[e];
     }
     return false;
 }
@@ -256,13 +318,16 @@ __device__ __forceinline__ void split_row_max(float (&m)[kRowTiles], int32_t j_b
                                               const half8 (&qop)[kRowTiles][8], int n, int qd) {
 #pragma unroll
     for (int rt = 0; rt < kRowTiles; ++rt) m[rt] = -INFINITY;
+    const int32_t last = j_end - 1;
     for (int32_t j0 = j_begin; j0 < j_end; j0 += kTileTokens) {
-        const TileAddr a = tile_addr(j0, j_end - 1, pages, pg0, kbase, vbase, p, n, qd);
+        const Granules gr = granules(j0, last, pages, pg0, kbase, vbase, p);
+        const uint8_t* rowA = gr.kA + (int64_t)(min(j0 + n, last) - j0) * p.k_token_stride + 16 * qd;
+        const uint8_t* rowB = gr.kB + (int64_t)(min(j0 + 16 + n, last) - gr.gsB) * p.k_token_stride + 16 * qd;
         TileK t;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            t.k[0][i] = *reinterpret_cast<const u32x4*>(a.kA + 64 * i);
-            t.k[1][i] = *reinterpret_cast<const u32x4*>(a.kB + 64 * i);
+            t.k[0][i] = *reinterpret_cast<const u32x4*>(rowA + 64 * i);
+            t.k[1][i] = *reinterpret_cast<const u32x4*>(rowB + 64 * i);
         }
         float4v sacc[2][kRowTiles];
         qk_tile(t, sacc, qop);
@@ -274,13 +339,13 @@ __device__ __forceinline__ void split_row_max(float (&m)[kRowTiles], int32_t j_b
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float v = sacc[tt][rt][i] * c;
+                    float v = sacc[tt][rt][i];
                     if (need_mask) v = (j0 + 16 * tt + 4 * qd + i) < lim[rt] ? v : -INFINITY;
                     mx = fmaxf(mx, v);
                 }
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            m[rt] = fmaxf(m[rt], mx);
+            m[rt] = fmaxf(m[rt], mx * c);
         }
     }
 }
@@ -290,11 +355,15 @@ __global__ __launch_bounds__(64) void split_kernel_e4m3_d256(RunParams p) {
     const int n = lane & 15;       // MFMA column = packed row within a row tile
     const int qd = lane >> 4;      // quarter of the wave
 
+    // Workgroup order: KV head fastest, then split, then slot. The KV heads of one token are
+    // adjacent in the cache (token stride = Hkv * head stride), so the workgroups that read the
+    // same tokens' rows are dispatched together and stream through the same DRAM pages at
+    // about the same time.
     int wg = blockIdx.x;
-    const int s = wg % p.grid_splits;
-    wg /= p.grid_splits;
     const int g = wg % p.num_kv_heads;
-    const int b = wg / p.num_kv_heads;
+    wg /= p.num_kv_heads;
+    const int s = wg % p.grid_splits;
+    const int b = wg / p.grid_splits;
 
     const int32_t L = clamp_len(p.seq_lens[b], p.max_seq_len);
     const int32_t S = num_splits(L, p.policy);
@@ -327,6 +396,19 @@ __global__ __launch_bounds__(64) void split_kernel_e4m3_d256(RunParams p) {
         const int32_t lr = p.causal ? (L - p.q_len + 1 + t) : L;
         lim[rt] = min(lr, j_end);
     }
+    // Score scale in log2 units, c = sm_scale * k_scale * log2(e). The softmax takes the max of
+    // the raw scores and scales it, which needs c > 0: a negative k_scale is moved into Q
+    // (negating FP16 is exact) and c = 0 is raised to the smallest normal float, which leaves
+    // every exp2 argument unchanged (|score| * 2^-126 rounds away) but keeps -inf * c = -inf.
+    float c = p.sm_scale * (*p.k_scale) * kLog2e;
+    if (c < 0.0f) {
+        c = -c;
+#pragma unroll
+        for (int rt = 0; rt < kRowTiles; ++rt)
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) qop[rt][ks] = -qop[rt][ks];
+    }
+    c = fmaxf(c, 1.17549435e-38f);
     // Make the Q loads land before the ring is primed: otherwise the compiler's waits for them,
     // placed at their first use, would count the ring loads issued in between and wait for those.
 #pragma unroll
@@ -334,7 +416,6 @@ __global__ __launch_bounds__(64) void split_kernel_e4m3_d256(RunParams p) {
 #pragma unroll
         for (int ks = 0; ks < 8; ks += 2) asm volatile("" ::"v"(qop[rt][ks]), "v"(qop[rt][ks + 1]));
     const int32_t mask_from = p.causal ? min(j_end, L - p.q_len + 1) : j_end;
-    const float c = p.sm_scale * (*p.k_scale) * kLog2e;   // scores in log2 units
 
     const uint8_t* kbase = p.k + (int64_t)g * p.k_head_stride;
     const uint8_t* vbase = p.v + (int64_t)g * p.v_head_stride;
@@ -361,6 +442,12 @@ __global__ __launch_bounds__(64) void split_kernel_e4m3_d256(RunParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t ring[2 * kStageBytes];
     const uint32_t ring0 = lds_addr(ring);
     const u32x4* ring_lane = reinterpret_cast<const u32x4*>(ring) + lane;
+    const LaneOffs lo = lane_offsets(p, lane, n, qd);
+    // LDS byte offsets of the consumer's K chunks: token n of granule tt at row 16*tt + n,
+    // chunk 4*i + qd (dims 64*i + 16*qd + 0..15) in slot chunk ^ n.
+    uint32_t k_rd[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) k_rd[i] = n * 256 + 16 * ((4 * i + qd) ^ n);
 
     // Per-row reference max (log2 units). A row's reference is the max of the first tile in
     // which it sees a key; exponentials are taken against it, so O and l never need
@@ -381,25 +468,29 @@ __global__ __launch_bounds__(64) void split_kernel_e4m3_d256(RunParams p) {
             for (int j = 0; j < 16; ++j) o[rt][j] = float4v{0.f, 0.f, 0.f, 0.f};
         }
         {
-            const TileAddr a0 = tile_addr(j_begin, last, pages, pg0, kbase, vbase, p, n, qd);
-            issue_k(a0, ring0);
-            issue_v(a0, ring0, qd, p.v_token_stride);
-            const TileAddr a1 = tile_addr(min(j_begin + kTileTokens, last_tile), last, pages, pg0, kbase, vbase, p, n, qd);
-            issue_k(a1, ring0 + kStageBytes);
-            issue_v(a1, ring0 + kStageBytes, qd, p.v_token_stride);
+            const Granules g0 = granules(j_begin, last, pages, pg0, kbase, vbase, p);
+            issue_k(g0, last, lo, ring0, p, lane);
+            issue_v(g0, last, lo, ring0, p, n, qd);
+            const Granules g1 = granules(min(j_begin + kTileTokens, last_tile), last, pages, pg0, kbase, vbase, p);
+            issue_k(g1, last, lo, ring0 + kStageBytes, p, lane);
+            issue_v(g1, last, lo, ring0 + kStageBytes, p, n, qd);
         }
         bool over = false;
         int32_t j0 = j_begin;
         for (int st = 0;; st ^= 1) {
             const uint32_t stage = ring0 + st * kStageBytes;
             const u32x4* sl = ring_lane + st * (kStageBytes / 16);
-            const TileAddr an = tile_addr(min(j0 + 2 * kTileTokens, last_tile), last, pages, pg0, kbase, vbase, p, n, qd);
+            const Granules gn = granules(min(j0 + 2 * kTileTokens, last_tile), last, pages, pg0, kbase, vbase, p);
             vm_wait_tile();
             TileK tk;
+            const uint8_t* stage_bytes = ring + st * kStageBytes;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) tk.k[i >> 2][i & 3] = sl[i * 64];
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    tk.k[tt][i] = *reinterpret_cast<const u32x4*>(stage_bytes + tt * 4096 + k_rd[i]);
             lds_wait_all();
-            issue_k(an, stage);
+            issue_k(gn, last, lo, stage, p, lane);
             float4v sacc[2][kRowTiles];
             qk_tile(tk, sacc, qop);
             half8 pop[kRowTiles];
@@ -408,7 +499,7 @@ __global__ __launch_bounds__(64) void split_kernel_e4m3_d256(RunParams p) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) tv.v[e] = sl[(8 + e) * 64];
             lds_wait_all();
-            issue_v(an, stage, qd, p.v_token_stride);
+            issue_v(gn, last, lo, stage, p, n, qd);
             if (over) break;
             pv_tile(tv, pop, o);
             j0 += kTileTokens;
@@ -452,8 +543,10 @@ __global__ __launch_bounds__(64) void split_kernel_e4m3_d256(RunParams p) {
     }
 }
 
-// Log-sum-exp combine: one wave per packed row, lanes cover 4 dims each. The splits of a row
-// are visited in index order, so the FP32 sums are bitwise reproducible.
+// Log-sum-exp combine: one wave per packed row. Lane s holds split s's (m, l) (splits past 64
+// are folded in by lane s % 64 in order), the max and the denominator are wave reductions, and
+// the O sum visits the splits in index order with every lane covering 4 dims; the split order
+// is fixed, so the FP32 sums are bitwise reproducible.
 __global__ __launch_bounds__(256) void combine_kernel_d256(RunParams p) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -471,27 +564,55 @@ __global__ __launch_bounds__(256) void combine_kernel_d256(RunParams p) {
     const int32_t L = clamp_len(p.seq_lens[b], p.max_seq_len);
     const int32_t S = num_splits(L, p.policy);
     const float* panel0 = p.ws + (int64_t)(b * p.num_kv_heads + g) * p.grid_splits * p.split_floats;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, panel0[(int64_t)s * p.split_floats + kRowsAlloc * kD + r]);
+    const int64_t m_off = kRowsAlloc * kD + r;
+    const int64_t l_off = kRowsAlloc * kD + kRowsAlloc + r;
+
+    float mloc = -INFINITY;
+    for (int s = lane; s < S; s += 64) mloc = fmaxf(mloc, panel0[(int64_t)s * p.split_floats + m_off]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
+    const float M = mloc;
+
     float4v acc = {0.f, 0.f, 0.f, 0.f};
     float den = 0.0f;
     if (M != -INFINITY) {
-        for (int s = 0; s < S; ++s) {
-            const float* panel = panel0 + (int64_t)s * p.split_floats;
-            const float ms = panel[kRowsAlloc * kD + r];
+        // weight and l of split `lane` (and lane + 64, ...), then the denominator
+        float dloc = 0.0f;
+        for (int s = lane; s < S; s += 64) {
+            const float ms = panel0[(int64_t)s * p.split_floats + m_off];
             const float w = ms == -INFINITY ? 0.0f : fast_exp2(ms - M);
-            den += w * panel[kRowsAlloc * kD + kRowsAlloc + r];
-            const float4v ov = *reinterpret_cast<const float4v*>(panel + r * kD + 4 * lane);
-            acc += w * ov;
+            dloc += w * panel0[(int64_t)s * p.split_floats + l_off];
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) dloc += __shfl_xor(dloc, off);
+        den = dloc;
+        const float* orow = panel0 + r * kD + 4 * lane;
+        int s = 0;
+        for (; s + 4 <= S; s += 4) {
+            float4v ov[4];
+            float w[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                ov[u] = *reinterpret_cast<const float4v*>(orow + (int64_t)(s + u) * p.split_floats);
+                const float ms = panel0[(int64_t)(s + u) * p.split_floats + m_off];
+                w[u] = ms == -INFINITY ? 0.0f : fast_exp2(ms - M);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc += w[u] * ov[u];
+        }
+        for (; s < S; ++s) {
+            const float4v ov = *reinterpret_cast<const float4v*>(orow + (int64_t)s * p.split_floats);
+            const float ms = panel0[(int64_t)s * p.split_floats + m_off];
+            acc += (ms == -INFINITY ? 0.0f : fast_exp2(ms - M)) * ov;
         }
     }
     const float scale = den > 0.0f ? (*p.v_scale) / den : 0.0f;
-    uint16_t* orow = p.out + (((int64_t)b * p.q_len + t) * p.num_q_heads + h) * kD + 4 * lane;
+    uint16_t* out = p.out + (((int64_t)b * p.q_len + t) * p.num_q_heads + h) * kD + 4 * lane;
     typedef _Float16 half4v __attribute__((ext_vector_type(4)));
     half4v res;
 #pragma unroll
     for (int i = 0; i < 4; ++i) res[i] = den > 0.0f ? (_Float16)(acc[i] * scale) : (_Float16)0.0f;
-    *reinterpret_cast<half4v*>(orow) = res;
+    *reinterpret_cast<half4v*>(out) = res;
 }
 
 }  // namespace
