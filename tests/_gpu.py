@@ -71,27 +71,8 @@ def compare(out: torch.Tensor, ref: np.ndarray, *, max_abs=MAX_ABS, rel_l2=REL_L
     return stats
 
 
-def sample_pairs_numpy(case: dict, pairs):
-    """Host copy of only the pages the sampled (b, g) pairs read, remapped, for the oracle."""
-    bt = case["block_table"].cpu()
-    lens = case["seq_lens"].cpu()
-    ps = case["page_size"]
-    need = sorted({int(p) for b, _ in pairs for p in bt[b, :-(-int(lens[b]) // ps)].tolist()})
-    remap = {p: i for i, p in enumerate(need)}
-    idx = torch.tensor(need, dtype=torch.long, device=case["k_cache"].device)
-    k = case["k_cache"].index_select(0, idx).cpu().numpy()
-    v = case["v_cache"].index_select(0, idx).cpu().numpy()
-    table = np.full(tuple(bt.shape), -1, dtype=np.int64)
-    for b in {b for b, _ in pairs}:
-        n = -(-int(lens[b]) // ps)
-        table[b, :n] = [remap[int(p)] for p in bt[b, :n].tolist()]
-    return dict(q=case["q"].cpu().numpy(), k_cache=k, v_cache=v, block_table=table, seq_lens=lens.numpy(),
-                k_scale=case["k_scale"].cpu().numpy(), v_scale=case["v_scale"].cpu().numpy(), page_size=ps,
-                kv_format=case["kv_format"])
-
-
 def oracle_pairs(case: dict, pairs, causal=True) -> np.ndarray:
-    c = sample_pairs_numpy(case, pairs)
+    c = wl.host_subset(case, pairs)
     return oracle.verify_attention(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"],
                                    float(c["k_scale"][0]), float(c["v_scale"][0]), page_size=c["page_size"],
                                    kv_format=c["kv_format"], causal=causal, pairs=pairs)

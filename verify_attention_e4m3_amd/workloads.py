@@ -191,6 +191,28 @@ def to_numpy(case: dict) -> dict:
     return out
 
 
+def host_subset(case: dict, pairs) -> dict:
+    """Host numpy copy of only the cache pages that the (slot, KV head) pairs read, with the
+    block table remapped onto them (so a large device case can be checked on the host)."""
+    import numpy as np
+    bt = case["block_table"].cpu()
+    lens = case["seq_lens"].cpu()
+    ps = case["page_size"]
+    slots = sorted({b for b, _ in pairs})
+    need = sorted({int(p) for b in slots for p in bt[b, :-(-int(lens[b]) // ps)].tolist()})
+    remap = {p: i for i, p in enumerate(need)}
+    idx = torch.tensor(need, dtype=torch.long, device=case["k_cache"].device)
+    k = case["k_cache"].index_select(0, idx).cpu().numpy()
+    v = case["v_cache"].index_select(0, idx).cpu().numpy()
+    table = np.full(tuple(bt.shape), -1, dtype=np.int64)
+    for b in slots:
+        n = -(-int(lens[b]) // ps)
+        table[b, :n] = [remap[int(p)] for p in bt[b, :n].tolist()]
+    return dict(q=case["q"].cpu().numpy(), k_cache=k, v_cache=v, block_table=table, seq_lens=lens.numpy(),
+                k_scale=case["k_scale"].cpu().numpy(), v_scale=case["v_scale"].cpu().numpy(), page_size=ps,
+                kv_format=case["kv_format"])
+
+
 def kv_bytes(seq_lens: Sequence[int], num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
     """Algorithmic KV bytes of one layer: every visible token's K and V row read once per KV head."""
     return int(sum(max(0, int(L)) for L in seq_lens)) * num_kv_heads * head_dim * 2 * elem_bytes
