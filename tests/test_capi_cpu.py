@@ -68,6 +68,7 @@ def test_capabilities():
     assert caps["max_seq_len"] == 262144
     assert caps["max_batch"] >= 32
     assert {"kv_dtype": A.ATTN_KV_E4M3, "head_dim": 256, "max_q_len": 8, "max_rows": 48} in caps["geometries"]
+    assert {"kv_dtype": A.ATTN_KV_FP16, "head_dim": 128, "max_q_len": 8, "max_rows": 48} in caps["geometries"]
 
 
 def test_status_strings():
@@ -102,7 +103,8 @@ def plan(**kw):
     (dict(sm_scale=float("inf")), A.ATTN_E_INVALID),
     (dict(abi_version=2), A.ATTN_E_INVALID),
     (dict(kv_dtype="e5m2"), A.ATTN_E_INVALID),
-    (dict(head_dim=128), A.ATTN_E_UNSUPPORTED),
+    (dict(head_dim=128), A.ATTN_E_UNSUPPORTED),                       # E4M3 at D128 is not built
+    (dict(kv_dtype="fp16"), A.ATTN_E_UNSUPPORTED),                     # FP16 at D256 is not built
     (dict(q_len=9, num_q_heads=4, num_kv_heads=4), A.ATTN_E_UNSUPPORTED),
     (dict(num_q_heads=28), A.ATTN_E_UNSUPPORTED),                       # G = 7 -> 56 rows > 48
 ])
@@ -116,6 +118,7 @@ def test_admission_rejects(kw, status):
     dict(), dict(page_size=16), dict(page_size=3296, max_seq_len=262144), dict(q_len=1, num_q_heads=4),
     dict(q_len=8, num_q_heads=4, num_kv_heads=1), dict(causal=False), dict(sm_scale=0.125),
     dict(k_strides=(1648 * 2056, 2056, 512), v_strides=(1648 * 2056, 2056, 512)),   # interleaved, 8-aligned
+    dict(kv_dtype="fp16", head_dim=128, q_len=1, num_q_heads=32, num_kv_heads=8),
 ])
 def test_admission_accepts(kw):
     p = plan(**kw)
@@ -162,8 +165,8 @@ def test_partitions_cover_each_row_exactly():
         assert P % info["partition_align"] == 0 and P % 32 == 0
         assert P >= info["partition_min"]
         assert (S - 1) * P < L <= S * P
-        assert 1 <= S <= info["split_cap"] <= info["grid_splits"] or S <= info["grid_splits"]
-        assert P <= 8192
+        assert 1 <= S <= info["split_cap"] and S <= info["grid_splits"]
+        assert P <= 16384
 
 
 def test_grid_covers_every_length():
@@ -171,6 +174,15 @@ def test_grid_covers_every_length():
     gs = p.info["grid_splits"]
     assert max(p.splits(L)[0] for L in range(0, 262145, 97)) <= gs
     assert max(p.splits(L)[0] for L in LENGTHS) <= gs
+
+
+@pytest.mark.parametrize("hkv,cap", [(1, 128), (2, 64), (4, 32), (8, 16), (32, 16)])
+def test_split_cap_follows_the_head_geometry(hkv, cap):
+    p = plan(num_q_heads=hkv * 6, num_kv_heads=hkv, max_seq_len=262144, page_size=3296)
+    assert p.info["split_cap"] == cap
+    for L in LENGTHS:
+        S, P = p.splits(L)
+        assert S <= cap and P <= 16384
 
 
 def test_split_policy_ignores_batch_and_page_size():
@@ -187,6 +199,15 @@ def test_long_rows_fill_the_chip():
     S, P = p.splits(131072)
     assert 8 * 4 * S == 4 * 256
     assert P == 4096
+
+
+def test_workspace_panel_holds_the_row_tiles():
+    # rows are held in tiles of 16: 48 rows at q8 G6, 16 rows at q1 G4 (D128)
+    big = plan()
+    small = plan(kv_dtype="fp16", head_dim=128, q_len=1, num_q_heads=32, num_kv_heads=8)
+    assert big.info["rows"] == 48 and small.info["rows"] == 4
+    assert big.info["split_bytes"] == -(-(48 * 256 + 96) * 4 // 256) * 256
+    assert small.info["split_bytes"] == -(-(16 * 128 + 32) * 4 // 256) * 256
 
 
 def test_workspace_is_request_major():

@@ -78,7 +78,36 @@ def test_parity_distinct_k_and_v_scales():
     compare(run_gpu(c), run_oracle(c))
 
 
-@pytest.mark.parametrize("name", ["verify_b1_ctx3297_hq6_hkv1", "verify_b4_ctx32k_gqa6"])
+FP16_D128 = [
+    dict(batch=2, seq_lens=[1, 3000], q_len=1, num_q_heads=8, num_kv_heads=2, page_size=16),
+    dict(batch=3, seq_lens=[40, 1649, 7], q_len=1, num_q_heads=32, num_kv_heads=8, page_size=1648),
+    dict(batch=2, seq_lens=[777, 5000], q_len=8, num_q_heads=16, num_kv_heads=4, page_size=32),   # 32 rows
+    dict(batch=2, seq_lens=[100, 2500], q_len=8, num_q_heads=48, num_kv_heads=8, page_size=64),   # 48 rows
+]
+
+
+@pytest.mark.parametrize("kw", FP16_D128, ids=lambda kw: f"fp16-B{kw['batch']}-L{max(kw['seq_lens'])}-q{kw['q_len']}-"
+                                                           f"H{kw['num_q_heads']}/{kw['num_kv_heads']}")
+def test_parity_fp16_d128(kw):
+    note(f"parity fp16 d128 {kw}")
+    c = _case(head_dim=128, kv_format="fp16", seed=sum(kw["seq_lens"]) + 3, **kw)
+    compare(run_gpu(c), run_oracle(c))
+
+
+def test_fp16_values_pass_through_exactly():
+    # q1, L = 1: the only key's V row comes out exactly (softmax of one key is 1).
+    note("fp16 d128 identity row")
+    c = _case(batch=1, seq_lens=[1], q_len=1, num_q_heads=4, num_kv_heads=1, head_dim=128, page_size=16,
+              kv_format="fp16", seed=5)
+    out = run_gpu(c)
+    page = int(c["block_table"][0, 0])
+    want = c["v_cache"][page, 0, 0, :]
+    for h in range(4):
+        assert torch.equal(out[0, 0, h], want), h
+
+
+@pytest.mark.parametrize("name", ["verify_b1_ctx3297_hq6_hkv1", "verify_b4_ctx32k_gqa6",
+                                  "decode_b8_ctx32k_d128_fp16_gqa4"])
 def test_parity_workload_full(name):
     note(f"parity full workload {name}")
     w = wl.WORKLOADS[name]

@@ -15,9 +15,9 @@
 
 namespace attn {
 
-// Row-tile geometry of the E4M3 D=256 kernel: 3 tiles of 16 packed rows (q_len * G <= 48).
-constexpr int kRowTiles = 3;
-constexpr int kRowsAlloc = 16 * kRowTiles;
+// Packed rows (q_len * G) are processed in tiles of 16, at most 3 tiles (48 rows).
+constexpr int kMaxRowTiles = 3;
+constexpr int kMaxRows = 16 * kMaxRowTiles;
 constexpr int kTileTokens = 32;        // tokens per inner iteration of one wave
 constexpr int kMaxBatch = 256;
 constexpr int kMaxSeqLen = 262144;
@@ -72,6 +72,7 @@ struct RunParams {
     int32_t num_kv_heads;
     int32_t group;                // Hq / Hkv
     int32_t rows;                 // q_len * group
+    int32_t rows_alloc;           // 16 * row tiles: rows held in a split panel
     int32_t grid_splits;          // splits per (slot, KV head) in the grid
     int32_t causal;
     int32_t split_floats;         // floats per split panel
@@ -89,6 +90,7 @@ struct attn_plan_s {
     attn::SplitPolicy policy;
     int32_t grid_splits;
     int32_t rows;
+    int32_t rows_alloc;
     float sm_scale;
     size_t split_floats;
     size_t split_bytes;

@@ -42,7 +42,6 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kD = 256;
 
 // Four E4M3 byte pairs -> eight FP16 values, byte k of (lo, hi) -> element k.
 __device__ __forceinline__ half8 e4m3x8(uint32_t lo, uint32_t hi) {
@@ -68,14 +67,95 @@ __device__ __forceinline__ int32_t clamp_len(int32_t L, int32_t max_len) {
 }
 
 constexpr float kRefSlack = 10.0f;
-// Block-table entries one split can touch: partitions are at most 8192 tokens and pages hold
-// at least 16 tokens, so a split spans at most 8192/16 + 1 pages.
-constexpr int kMaxSplitPages = 8192 / 16 + 2;
+// Block-table entries one split can touch: partitions are at most 16384 tokens and pages hold
+// at least 16 tokens, so a split spans at most 16384/16 + 1 pages.
+constexpr int kMaxSplitPages = 16384 / 16 + 2;
 
-// One 32-token tile as each lane holds it. K: granule tt (tokens j0 + 16*tt + n), dims
-// 64*i + 16*qd + 0..15. V: slot e = token 4*qd + (e & 3) of granule e >> 2, dims 16*n + 0..15.
+// One 32-token tile as each lane holds it (see LaneOffs for which bytes).
 struct TileK { u32x4 k[2][4]; };
 struct TileV { u32x4 v[8]; };
+
+// KV element formats whose token rows of one head are 256 bytes: E4M3 at D = 256 and FP16 at
+// D = 128. They share the gather, the LDS ring and the swizzle; they differ in how a lane's 16
+// bytes become MFMA operands and which output dims an accumulator element holds.
+enum KvFormat { kFmtE4M3D256 = 0, kFmtF16D128 = 1 };
+
+template <int FMT> struct Fmt;
+
+// E4M3, D = 256. K vector i of a lane holds dims 64*i + 16*qd + 0..15 (one byte each) and
+// feeds k-steps 2i and 2i+1; PV MFMA j (0..15) covers dims 16*m + j.
+template <> struct Fmt<kFmtE4M3D256> {
+    static constexpr int D = 256;
+    static constexpr int KSTEPS = 8;
+    static constexpr int JT = 16;
+    __device__ static int q_dim(int ks, int qd) { return 64 * (ks >> 1) + 16 * qd + 8 * (ks & 1); }
+    __device__ static half8 k_op(const u32x4 (&k)[4], int ks) {
+        const u32x4 w = k[ks >> 1];
+        return (ks & 1) ? e4m3x8(w[2], w[3]) : e4m3x8(w[0], w[1]);
+    }
+    __device__ static int o_dim(int qd, int i, int j) { return 16 * (4 * qd + i) + j; }
+    // O^T += V^T . P^T. For dword w of the lane's 16 V bytes and byte pair (2cp, 2cp+1), a byte
+    // permute regroups tokens (2pp, 2pp+1) of dims 16*n + 4*w + 2*cp + {0,1} into 16-bit words,
+    // which convert to the FP16 pairs of the A operand.
+    template <int RT>
+    __device__ static void pv(const TileV& t, const half8 (&pop)[RT], float4v (&o)[RT][JT]) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+#pragma unroll
+            for (int cp = 0; cp < 2; ++cp) {
+                const uint32_t sel = cp ? 0x07030602u : 0x05010400u;
+                half8 a0, a1;
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp) {
+                    const uint32_t pr = __builtin_amdgcn_perm(t.v[2 * pp + 1][w], t.v[2 * pp][w], sel);
+                    const half2v lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pr, 1.0f, false);
+                    const half2v hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pr, 1.0f, true);
+                    a0[2 * pp] = lo[0];
+                    a0[2 * pp + 1] = lo[1];
+                    a1[2 * pp] = hi[0];
+                    a1[2 * pp + 1] = hi[1];
+                }
+                const int jd = 4 * w + 2 * cp;
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    o[rt][jd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, pop[rt], o[rt][jd], 0, 0, 0);
+                    o[rt][jd + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, pop[rt], o[rt][jd + 1], 0, 0, 0);
+                }
+            }
+        }
+    }
+};
+
+// FP16, D = 128. K vector i of a lane holds dims 32*i + 8*qd + 0..7 and is k-step i as it is;
+// PV MFMA j (0..7) covers dims 8*m + j.
+template <> struct Fmt<kFmtF16D128> {
+    static constexpr int D = 128;
+    static constexpr int KSTEPS = 4;
+    static constexpr int JT = 8;
+    __device__ static int q_dim(int ks, int qd) { return 32 * ks + 8 * qd; }
+    __device__ static half8 k_op(const u32x4 (&k)[4], int ks) { return __builtin_bit_cast(half8, k[ks]); }
+    __device__ static int o_dim(int qd, int i, int j) { return 8 * (4 * qd + i) + j; }
+    // O^T += V^T . P^T. Dword w of the lane's 16 V bytes holds dims 8*n + 2w, 2w+1 of a token;
+    // a permute pairs tokens (2pp, 2pp+1) of one of those dims into an FP16 pair.
+    template <int RT>
+    __device__ static void pv(const TileV& t, const half8 (&pop)[RT], float4v (&o)[RT][JT]) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t sel = h ? 0x07060302u : 0x05040100u;
+                u32x4 a;
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp) a[pp] = __builtin_amdgcn_perm(t.v[2 * pp + 1][w], t.v[2 * pp][w], sel);
+                const half8 ah = __builtin_bit_cast(half8, a);
+                const int jd = 2 * w + h;
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    o[rt][jd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, pop[rt], o[rt][jd], 0, 0, 0);
+            }
+        }
+    }
+};
 
 // Page and slot of logical token j (a granule start): j / page_size by a multiply-shift with
 // the host-computed reciprocal ceil(2^40 / page_size), exact for j < 2^20 and page_size < 2^20.
@@ -119,11 +199,14 @@ struct Granules {
     const uint8_t* vA;
     const uint8_t* vB;
     int32_t j0, gsB;
+    bool past_end;       // a prefetch beyond the split: every lane re-reads token `last`
 };
 
 __device__ __forceinline__ Granules granules(int32_t j0, int32_t last, const int32_t* pages, int32_t pg0,
                                              const uint8_t* kbase, const uint8_t* vbase, const RunParams& p) {
     Granules gr;
+    gr.past_end = j0 > last;
+    if (gr.past_end) j0 = last & ~15;
     gr.j0 = j0;
     gr.gsB = min(j0 + 16, last & ~15);
     int32_t ia, sa, ib, sb;
@@ -157,10 +240,12 @@ constexpr int kStageRows = 16;
 constexpr int kStageBytes = kStageRows * 64 * 16;
 
 // A tile whose 32 tokens all precede `last` uses the split's fixed lane offsets; the tail tile
-// clamps each lane's token to `last` (whose page exists; the extra tokens are masked).
+// clamps each lane's token to `last` (whose page exists; the extra tokens are masked). A
+// prefetch past the split's end keeps the per-tile load count (so the ring's vmcnt accounting
+// is the same every iteration) but reads only token `last`'s row, which stays in L2.
 __device__ __forceinline__ void issue_k(const Granules& gr, int32_t last, const LaneOffs& lo, uint32_t stage,
                                         const RunParams& p, int lane) {
-    if (gr.j0 + kTileTokens - 1 <= last) {
+    if (gr.j0 + kTileTokens - 1 <= last && !gr.past_end) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             dma16(gr.kA, lo.k[i], stage + i * 1024);
@@ -168,21 +253,24 @@ __device__ __forceinline__ void issue_k(const Granules& gr, int32_t last, const 
         }
     } else {
         const int tr = lane >> 4, slot = lane & 15;
+        const int32_t cap = gr.past_end ? gr.j0 : last;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int tok = 4 * i + tr;
-            const uint32_t oa = (uint32_t)((min(gr.j0 + tok, last) - gr.j0) * p.k_token_stride + 16 * (slot ^ tok));
+            const uint32_t oa =
+                (uint32_t)((min(gr.j0 + tok, last) - gr.j0) * p.k_token_stride + 16 * (slot ^ tok));
             const uint32_t ob =
                 (uint32_t)((min(gr.j0 + 16 + tok, last) - gr.gsB) * p.k_token_stride + 16 * (slot ^ tok));
-            dma16(gr.kA, oa, stage + i * 1024);
-            dma16(gr.kB, ob, stage + (4 + i) * 1024);
+            dma16(gr.kA, gr.past_end ? (uint32_t)((last - cap) * p.k_token_stride + 16 * slot) : oa, stage + i * 1024);
+            dma16(gr.kB, gr.past_end ? (uint32_t)((last - cap) * p.k_token_stride + 16 * slot) : ob,
+                  stage + (4 + i) * 1024);
         }
     }
 }
 
 __device__ __forceinline__ void issue_v(const Granules& gr, int32_t last, const LaneOffs& lo, uint32_t stage,
                                         const RunParams& p, int n, int qd) {
-    if (gr.j0 + kTileTokens - 1 <= last) {
+    if (gr.j0 + kTileTokens - 1 <= last && !gr.past_end) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             dma16(gr.vA, lo.v[e], stage + (8 + e) * 1024);
@@ -194,8 +282,9 @@ __device__ __forceinline__ void issue_v(const Granules& gr, int32_t last, const 
             const int rel = 4 * qd + e;
             const uint32_t oa = (uint32_t)((min(gr.j0 + rel, last) - gr.j0) * p.v_token_stride + 16 * n);
             const uint32_t ob = (uint32_t)((min(gr.j0 + 16 + rel, last) - gr.gsB) * p.v_token_stride + 16 * n);
-            dma16(gr.vA, oa, stage + (8 + e) * 1024);
-            dma16(gr.vB, ob, stage + (12 + e) * 1024);
+            const uint32_t oz = (uint32_t)((last - gr.j0) * p.v_token_stride + 16 * n);
+            dma16(gr.vA, gr.past_end ? oz : oa, stage + (8 + e) * 1024);
+            dma16(gr.vB, gr.past_end ? oz : ob, stage + (12 + e) * 1024);
         }
     }
 }
@@ -204,21 +293,20 @@ __device__ __forceinline__ void vm_wait_tile() { asm volatile("s_waitcnt vmcnt(1
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// S^T = K . Q^T for the tile's two 16-token granules and the three row tiles.
-__device__ __forceinline__ void qk_tile(const TileK& t, float4v (&sacc)[2][kRowTiles],
-                                        const half8 (&qop)[kRowTiles][8]) {
+// S^T = K . Q^T for the tile's two 16-token granules and the row tiles.
+template <int FMT, int RT>
+__device__ __forceinline__ void qk_tile(const TileK& t, float4v (&sacc)[2][RT], const half8 (&qop)[RT][Fmt<FMT>::KSTEPS]) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int rt = 0; rt < kRowTiles; ++rt) sacc[tt][rt] = float4v{0.f, 0.f, 0.f, 0.f};
+        for (int rt = 0; rt < RT; ++rt) sacc[tt][rt] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < Fmt<FMT>::KSTEPS; ++ks) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            const u32x4 w = t.k[tt][ks >> 1];
-            const half8 a = (ks & 1) ? e4m3x8(w[2], w[3]) : e4m3x8(w[0], w[1]);
+            const half8 a = Fmt<FMT>::k_op(t.k[tt], ks);
 #pragma unroll
-            for (int rt = 0; rt < kRowTiles; ++rt)
+            for (int rt = 0; rt < RT; ++rt)
                 sacc[tt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qop[rt][ks], sacc[tt][rt], 0, 0, 0);
         }
     }
@@ -228,29 +316,30 @@ __device__ __forceinline__ void qk_tile(const TileK& t, float4v (&sacc)[2][kRowT
 // exponentials exp2(c*x - m) against the row references (c > 0, log2 units), P^T in FP16.
 // Returns true (uniformly) when a row's tile max exceeds its reference by more than kRefSlack;
 // the references are then raised and nothing was accumulated.
-__device__ __forceinline__ bool softmax_tile(const float4v (&sacc)[2][kRowTiles], int32_t j0, int32_t mask_from,
-                                             const int32_t (&lim)[kRowTiles], float c, float (&m_ref)[kRowTiles],
-                                             float (&l_run)[kRowTiles], half8 (&pop)[kRowTiles], int qd) {
-    float x[kRowTiles][8];
+template <int RT>
+__device__ __forceinline__ bool softmax_tile(const float4v (&sacc)[2][RT], int32_t j0, int32_t mask_from,
+                                             const int32_t (&lim)[RT], float c, float (&m_ref)[RT],
+                                             float (&l_run)[RT], half8 (&pop)[RT], int qd) {
+    float x[RT][8];
 #pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) x[rt][tt * 4 + i] = sacc[tt][rt][i];
     if (j0 + kTileTokens > mask_from) {      // only tiles at the causal tail or the row end
 #pragma unroll
-        for (int rt = 0; rt < kRowTiles; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     x[rt][tt * 4 + i] = (j0 + 16 * tt + 4 * qd + i) < lim[rt] ? x[rt][tt * 4 + i] : -INFINITY;
     }
-    float mx[kRowTiles];
+    float mx[RT];
     bool over = false;
 #pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
         float m = max3f(max3f(x[rt][0], x[rt][1], x[rt][2]), max3f(x[rt][3], x[rt][4], x[rt][5]),
                         max3f(x[rt][6], x[rt][7], x[rt][7]));
         const float m16 = __shfl_xor(m, 16);
@@ -263,11 +352,11 @@ __device__ __forceinline__ bool softmax_tile(const float4v (&sacc)[2][kRowTiles]
     }
     if (__any(over)) {
 #pragma unroll
-        for (int rt = 0; rt < kRowTiles; ++rt) m_ref[rt] = fmaxf(m_ref[rt], mx[rt]);
+        for (int rt = 0; rt < RT; ++rt) m_ref[rt] = fmaxf(m_ref[rt], mx[rt]);
         return true;
     }
 #pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
         if (m_ref[rt] == -INFINITY) m_ref[rt] = mx[rt];        // first tile with a visible key
         const float neg_m = m_ref[rt] == -INFINITY ? 0.0f : -m_ref[rt];
         float pe[8];
@@ -280,44 +369,15 @@ __device__ __forceinline__ bool softmax_tile(const float4v (&sacc)[2][kRowTiles]
     return false;
 }
 
-// O^T += V^T . P^T. For dword w of the lane's 16 V bytes and byte pair (2cp, 2cp+1), a byte
-// permute regroups tokens (2pp, 2pp+1) of dims 16*n + 4*w + 2*cp + {0,1} into 16-bit words,
-// which convert to the FP16 pairs of the A operand.
-__device__ __forceinline__ void pv_tile(const TileV& t, const half8 (&pop)[kRowTiles], float4v (&o)[kRowTiles][16]) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-#pragma unroll
-        for (int cp = 0; cp < 2; ++cp) {
-            const uint32_t sel = cp ? 0x07030602u : 0x05010400u;
-            half8 a0, a1;
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-                const uint32_t pr = __builtin_amdgcn_perm(t.v[2 * pp + 1][w], t.v[2 * pp][w], sel);
-                const half2v lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pr, 1.0f, false);
-                const half2v hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pr, 1.0f, true);
-                a0[2 * pp] = lo[0];
-                a0[2 * pp + 1] = lo[1];
-                a1[2 * pp] = hi[0];
-                a1[2 * pp + 1] = hi[1];
-            }
-            const int jd = 4 * w + 2 * cp;
-#pragma unroll
-            for (int rt = 0; rt < kRowTiles; ++rt) {
-                o[rt][jd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, pop[rt], o[rt][jd], 0, 0, 0);
-                o[rt][jd + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, pop[rt], o[rt][jd + 1], 0, 0, 0);
-            }
-        }
-    }
-}
-
 // Exact maximum of every row's scaled, masked scores over the split (log2 units; -inf for a
 // row that sees no key in it). Used only by the rare recompute of a split; plain global loads.
-__device__ __forceinline__ void split_row_max(float (&m)[kRowTiles], int32_t j_begin, int32_t j_end, int32_t mask_from,
-                                              const int32_t (&lim)[kRowTiles], float c, const int32_t* pages,
-                                              int32_t pg0, const uint8_t* kbase, const uint8_t* vbase, const RunParams& p,
-                                              const half8 (&qop)[kRowTiles][8], int n, int qd) {
+template <int FMT, int RT>
+__device__ __forceinline__ void split_row_max(float (&m)[RT], int32_t j_begin, int32_t j_end, int32_t mask_from,
+                                              const int32_t (&lim)[RT], float c, const int32_t* pages, int32_t pg0,
+                                              const uint8_t* kbase, const uint8_t* vbase, const RunParams& p,
+                                              const half8 (&qop)[RT][Fmt<FMT>::KSTEPS], int n, int qd) {
 #pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt) m[rt] = -INFINITY;
+    for (int rt = 0; rt < RT; ++rt) m[rt] = -INFINITY;
     const int32_t last = j_end - 1;
     for (int32_t j0 = j_begin; j0 < j_end; j0 += kTileTokens) {
         const Granules gr = granules(j0, last, pages, pg0, kbase, vbase, p);
@@ -329,11 +389,11 @@ __device__ __forceinline__ void split_row_max(float (&m)[kRowTiles], int32_t j_b
             t.k[0][i] = *reinterpret_cast<const u32x4*>(rowA + 64 * i);
             t.k[1][i] = *reinterpret_cast<const u32x4*>(rowB + 64 * i);
         }
-        float4v sacc[2][kRowTiles];
-        qk_tile(t, sacc, qop);
+        float4v sacc[2][RT];
+        qk_tile<FMT, RT>(t, sacc, qop);
         const bool need_mask = j0 + kTileTokens > mask_from;
 #pragma unroll
-        for (int rt = 0; rt < kRowTiles; ++rt) {
+        for (int rt = 0; rt < RT; ++rt) {
             float mx = -INFINITY;
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
@@ -350,7 +410,13 @@ __device__ __forceinline__ void split_row_max(float (&m)[kRowTiles], int32_t j_b
     }
 }
 
-__global__ __launch_bounds__(64) void split_kernel_e4m3_d256(RunParams p) {
+// Split kernel: one 64-lane wave per (slot, KV head, split); RT row tiles of 16 packed rows.
+template <int FMT, int RT>
+__global__ __launch_bounds__(64) void split_kernel(RunParams p) {
+    using F = Fmt<FMT>;
+    constexpr int D = F::D;
+    constexpr int KS = F::KSTEPS;
+    constexpr int JT = F::JT;
     const int lane = threadIdx.x;
     const int n = lane & 15;       // MFMA column = packed row within a row tile
     const int qd = lane >> 4;      // quarter of the wave
@@ -372,24 +438,22 @@ __global__ __launch_bounds__(64) void split_kernel_e4m3_d256(RunParams p) {
     const int32_t j_begin = s * P;
     const int32_t j_end = min(j_begin + P, L);
     const int32_t last = j_end - 1;
-    const int32_t last_tile = j_begin + (last - j_begin) / kTileTokens * kTileTokens;
 
-    // Q^T operands stay in registers for the whole split: entry (rt, ks) holds dims
-    // 64*(ks/2) + 16*qd + 8*(ks%2) + 0..7 of packed row rt*16 + n (zeros past q_len*G) - the
-    // dim order of the K operand, so the contraction pairs matching dims.
-    half8 qop[kRowTiles][8];
-    int32_t lim[kRowTiles];
+    // Q^T operands stay in registers for the whole split: entry (rt, ks) holds the 8 dims of
+    // k-step ks (F::q_dim) of packed row rt*16 + n (zeros past q_len*G) - the dim order of the
+    // K operand, so the contraction pairs matching dims.
+    half8 qop[RT][KS];
+    int32_t lim[RT];
 #pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
         const int r = rt * 16 + n;
         const int t = r / p.group;
         const int h = g * p.group + (r - t * p.group);
         const bool live = r < p.rows;
-        const uint16_t* qrow = p.q + (((int64_t)b * p.q_len + (live ? t : 0)) * p.num_q_heads + (live ? h : 0)) * kD;
+        const uint16_t* qrow = p.q + (((int64_t)b * p.q_len + (live ? t : 0)) * p.num_q_heads + (live ? h : 0)) * D;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const int d0 = 64 * (ks >> 1) + 16 * qd + 8 * (ks & 1);
-            const half8 v = *reinterpret_cast<const half8*>(qrow + d0);
+        for (int ks = 0; ks < KS; ++ks) {
+            const half8 v = *reinterpret_cast<const half8*>(qrow + F::q_dim(ks, qd));
             qop[rt][ks] = live ? v : half8{0, 0, 0, 0, 0, 0, 0, 0};
         }
         // Keys j < lim are visible to this row: the verify token t sits at position L - q_len + t.
@@ -404,17 +468,17 @@ __global__ __launch_bounds__(64) void split_kernel_e4m3_d256(RunParams p) {
     if (c < 0.0f) {
         c = -c;
 #pragma unroll
-        for (int rt = 0; rt < kRowTiles; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) qop[rt][ks] = -qop[rt][ks];
+            for (int ks = 0; ks < KS; ++ks) qop[rt][ks] = -qop[rt][ks];
     }
     c = fmaxf(c, 1.17549435e-38f);
     // Make the Q loads land before the ring is primed: otherwise the compiler's waits for them,
     // placed at their first use, would count the ring loads issued in between and wait for those.
 #pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int ks = 0; ks < 8; ks += 2) asm volatile("" ::"v"(qop[rt][ks]), "v"(qop[rt][ks + 1]));
+        for (int ks = 0; ks < KS; ks += 2) asm volatile("" ::"v"(qop[rt][ks]), "v"(qop[rt][ks + 1]));
     const int32_t mask_from = p.causal ? min(j_end, L - p.q_len + 1) : j_end;
 
     const uint8_t* kbase = p.k + (int64_t)g * p.k_head_stride;
@@ -444,7 +508,7 @@ __global__ __launch_bounds__(64) void split_kernel_e4m3_d256(RunParams p) {
     const u32x4* ring_lane = reinterpret_cast<const u32x4*>(ring) + lane;
     const LaneOffs lo = lane_offsets(p, lane, n, qd);
     // LDS byte offsets of the consumer's K chunks: token n of granule tt at row 16*tt + n,
-    // chunk 4*i + qd (dims 64*i + 16*qd + 0..15) in slot chunk ^ n.
+    // chunk 4*i + qd in slot chunk ^ n.
     uint32_t k_rd[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) k_rd[i] = n * 256 + 16 * ((4 * i + qd) ^ n);
@@ -456,22 +520,22 @@ __global__ __launch_bounds__(64) void split_kernel_e4m3_d256(RunParams p) {
     // exceeds it by more, the split is recomputed once with each row's exact maximum over the
     // split as its reference (then no tile can exceed it). Both passes depend only on the
     // split's own data, so the result is deterministic.
-    float m_ref[kRowTiles];
-    float l_run[kRowTiles];
-    float4v o[kRowTiles][16];
+    float m_ref[RT];
+    float l_run[RT];
+    float4v o[RT][JT];
 
     auto run_pass = [&]() -> bool {
 #pragma unroll
-        for (int rt = 0; rt < kRowTiles; ++rt) {
+        for (int rt = 0; rt < RT; ++rt) {
             l_run[rt] = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) o[rt][j] = float4v{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < JT; ++j) o[rt][j] = float4v{0.f, 0.f, 0.f, 0.f};
         }
         {
             const Granules g0 = granules(j_begin, last, pages, pg0, kbase, vbase, p);
             issue_k(g0, last, lo, ring0, p, lane);
             issue_v(g0, last, lo, ring0, p, n, qd);
-            const Granules g1 = granules(min(j_begin + kTileTokens, last_tile), last, pages, pg0, kbase, vbase, p);
+            const Granules g1 = granules(j_begin + kTileTokens, last, pages, pg0, kbase, vbase, p);
             issue_k(g1, last, lo, ring0 + kStageBytes, p, lane);
             issue_v(g1, last, lo, ring0 + kStageBytes, p, n, qd);
         }
@@ -480,7 +544,7 @@ __global__ __launch_bounds__(64) void split_kernel_e4m3_d256(RunParams p) {
         for (int st = 0;; st ^= 1) {
             const uint32_t stage = ring0 + st * kStageBytes;
             const u32x4* sl = ring_lane + st * (kStageBytes / 16);
-            const Granules gn = granules(min(j0 + 2 * kTileTokens, last_tile), last, pages, pg0, kbase, vbase, p);
+            const Granules gn = granules(j0 + 2 * kTileTokens, last, pages, pg0, kbase, vbase, p);
             vm_wait_tile();
             TileK tk;
             const uint8_t* stage_bytes = ring + st * kStageBytes;
@@ -491,17 +555,17 @@ __global__ __launch_bounds__(64) void split_kernel_e4m3_d256(RunParams p) {
                     tk.k[tt][i] = *reinterpret_cast<const u32x4*>(stage_bytes + tt * 4096 + k_rd[i]);
             lds_wait_all();
             issue_k(gn, last, lo, stage, p, lane);
-            float4v sacc[2][kRowTiles];
-            qk_tile(tk, sacc, qop);
-            half8 pop[kRowTiles];
-            over = softmax_tile(sacc, j0, mask_from, lim, c, m_ref, l_run, pop, qd);
+            float4v sacc[2][RT];
+            qk_tile<FMT, RT>(tk, sacc, qop);
+            half8 pop[RT];
+            over = softmax_tile<RT>(sacc, j0, mask_from, lim, c, m_ref, l_run, pop, qd);
             TileV tv;
 #pragma unroll
             for (int e = 0; e < 8; ++e) tv.v[e] = sl[(8 + e) * 64];
             lds_wait_all();
             issue_v(gn, last, lo, stage, p, n, qd);
             if (over) break;
-            pv_tile(tv, pop, o);
+            F::template pv<RT>(tv, pop, o);
             j0 += kTileTokens;
             if (j0 > last) break;
         }
@@ -509,35 +573,37 @@ __global__ __launch_bounds__(64) void split_kernel_e4m3_d256(RunParams p) {
         return over;
     };
 
+    const int rows_alloc = 16 * RT;
     float* panel = p.ws + ((int64_t)(b * p.num_kv_heads + g) * p.grid_splits + s) * p.split_floats;
-    // Split epilogue: O^T tile j holds O[row n][dim 16*(4*qd + i) + j] in element i.
+    // Split epilogue: O^T tile j holds O[row n][dim F::o_dim(qd, i, j)] in element i; for a fixed
+    // i, groups of 4 consecutive j are 4 consecutive dims.
     auto store_panel = [&]() {
 #pragma unroll
-        for (int rt = 0; rt < kRowTiles; ++rt) {
+        for (int rt = 0; rt < RT; ++rt) {
             const int r = rt * 16 + n;
-            float* orow = panel + r * kD + 64 * qd;
+            float* orow = panel + r * D;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int c4 = 0; c4 < 4; ++c4)
-                    *reinterpret_cast<float4v*>(orow + 16 * i + 4 * c4) =
+                for (int c4 = 0; c4 < JT / 4; ++c4)
+                    *reinterpret_cast<float4v*>(orow + F::o_dim(qd, i, 4 * c4)) =
                         float4v{o[rt][4 * c4][i], o[rt][4 * c4 + 1][i], o[rt][4 * c4 + 2][i], o[rt][4 * c4 + 3][i]};
             float l = l_run[rt];
             l += __shfl_xor(l, 16);
             l += __shfl_xor(l, 32);
             if (qd == 0) {
-                panel[kRowsAlloc * kD + r] = m_ref[rt];
-                panel[kRowsAlloc * kD + kRowsAlloc + r] = l;
+                panel[rows_alloc * D + r] = m_ref[rt];
+                panel[rows_alloc * D + rows_alloc + r] = l;
             }
         }
     };
 
 #pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt) m_ref[rt] = -INFINITY;
+    for (int rt = 0; rt < RT; ++rt) m_ref[rt] = -INFINITY;
     const bool over = run_pass();
     store_panel();
     if (over) {
-        split_row_max(m_ref, j_begin, j_end, mask_from, lim, c, pages, pg0, kbase, vbase, p, qop, n, qd);
+        split_row_max<FMT, RT>(m_ref, j_begin, j_end, mask_from, lim, c, pages, pg0, kbase, vbase, p, qop, n, qd);
         run_pass();
         store_panel();
     }
@@ -545,9 +611,13 @@ __global__ __launch_bounds__(64) void split_kernel_e4m3_d256(RunParams p) {
 
 // Log-sum-exp combine: one wave per packed row. Lane s holds split s's (m, l) (splits past 64
 // are folded in by lane s % 64 in order), the max and the denominator are wave reductions, and
-// the O sum visits the splits in index order with every lane covering 4 dims; the split order
-// is fixed, so the FP32 sums are bitwise reproducible.
-__global__ __launch_bounds__(256) void combine_kernel_d256(RunParams p) {
+// the O sum visits the splits in index order with every lane covering D/64 dims; the split
+// order is fixed, so the FP32 sums are bitwise reproducible.
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(RunParams p) {
+    constexpr int VW = D / 64;
+    typedef float floatv __attribute__((ext_vector_type(VW)));
+    typedef _Float16 halfv __attribute__((ext_vector_type(VW)));
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int row_blocks = (p.rows + 3) / 4;
@@ -564,8 +634,8 @@ __global__ __launch_bounds__(256) void combine_kernel_d256(RunParams p) {
     const int32_t L = clamp_len(p.seq_lens[b], p.max_seq_len);
     const int32_t S = num_splits(L, p.policy);
     const float* panel0 = p.ws + (int64_t)(b * p.num_kv_heads + g) * p.grid_splits * p.split_floats;
-    const int64_t m_off = kRowsAlloc * kD + r;
-    const int64_t l_off = kRowsAlloc * kD + kRowsAlloc + r;
+    const int64_t m_off = (int64_t)p.rows_alloc * D + r;
+    const int64_t l_off = m_off + p.rows_alloc;
 
     float mloc = -INFINITY;
     for (int s = lane; s < S; s += 64) mloc = fmaxf(mloc, panel0[(int64_t)s * p.split_floats + m_off]);
@@ -573,10 +643,9 @@ __global__ __launch_bounds__(256) void combine_kernel_d256(RunParams p) {
     for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
     const float M = mloc;
 
-    float4v acc = {0.f, 0.f, 0.f, 0.f};
+    floatv acc = {};
     float den = 0.0f;
     if (M != -INFINITY) {
-        // weight and l of split `lane` (and lane + 64, ...), then the denominator
         float dloc = 0.0f;
         for (int s = lane; s < S; s += 64) {
             const float ms = panel0[(int64_t)s * p.split_floats + m_off];
@@ -586,14 +655,14 @@ __global__ __launch_bounds__(256) void combine_kernel_d256(RunParams p) {
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) dloc += __shfl_xor(dloc, off);
         den = dloc;
-        const float* orow = panel0 + r * kD + 4 * lane;
+        const float* orow = panel0 + r * D + VW * lane;
         int s = 0;
         for (; s + 4 <= S; s += 4) {
-            float4v ov[4];
+            floatv ov[4];
             float w[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                ov[u] = *reinterpret_cast<const float4v*>(orow + (int64_t)(s + u) * p.split_floats);
+                ov[u] = *reinterpret_cast<const floatv*>(orow + (int64_t)(s + u) * p.split_floats);
                 const float ms = panel0[(int64_t)(s + u) * p.split_floats + m_off];
                 w[u] = ms == -INFINITY ? 0.0f : fast_exp2(ms - M);
             }
@@ -601,18 +670,28 @@ __global__ __launch_bounds__(256) void combine_kernel_d256(RunParams p) {
             for (int u = 0; u < 4; ++u) acc += w[u] * ov[u];
         }
         for (; s < S; ++s) {
-            const float4v ov = *reinterpret_cast<const float4v*>(orow + (int64_t)s * p.split_floats);
+            const floatv ov = *reinterpret_cast<const floatv*>(orow + (int64_t)s * p.split_floats);
             const float ms = panel0[(int64_t)s * p.split_floats + m_off];
             acc += (ms == -INFINITY ? 0.0f : fast_exp2(ms - M)) * ov;
         }
     }
     const float scale = den > 0.0f ? (*p.v_scale) / den : 0.0f;
-    uint16_t* out = p.out + (((int64_t)b * p.q_len + t) * p.num_q_heads + h) * kD + 4 * lane;
-    typedef _Float16 half4v __attribute__((ext_vector_type(4)));
-    half4v res;
+    uint16_t* out = p.out + (((int64_t)b * p.q_len + t) * p.num_q_heads + h) * D + VW * lane;
+    halfv res;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) res[i] = den > 0.0f ? (_Float16)(acc[i] * scale) : (_Float16)0.0f;
-    *reinterpret_cast<half4v*>(out) = res;
+    for (int i = 0; i < VW; ++i) res[i] = den > 0.0f ? (_Float16)(acc[i] * scale) : (_Float16)0.0f;
+    *reinterpret_cast<halfv*>(out) = res;
+}
+
+typedef void (*KernelFn)(RunParams);
+
+template <int FMT>
+KernelFn split_for_rows(int row_tiles) {
+    switch (row_tiles) {
+        case 1: return split_kernel<FMT, 1>;
+        case 2: return split_kernel<FMT, 2>;
+        default: return split_kernel<FMT, 3>;
+    }
 }
 
 }  // namespace
@@ -621,20 +700,21 @@ __global__ __launch_bounds__(256) void combine_kernel_d256(RunParams p) {
 attn_status attn_launch_split(const attn_plan_s* plan, const attn::RunParams& p, void* stream) {
     attn::RunParams args = p;
     void* kargs[] = {&args};
+    const int row_tiles = p.rows_alloc / 16;
+    attn::KernelFn fn = plan->desc.kv_dtype == ATTN_KV_FP16 ? attn::split_for_rows<attn::kFmtF16D128>(row_tiles)
+                                                             : attn::split_for_rows<attn::kFmtE4M3D256>(row_tiles);
     const unsigned grid = (unsigned)p.batch * p.num_kv_heads * p.grid_splits;
-    hipError_t e = hipLaunchKernel((const void*)attn::split_kernel_e4m3_d256, dim3(grid), dim3(64), kargs, 0,
-                                   (hipStream_t)stream);
-    (void)plan;
+    hipError_t e = hipLaunchKernel((const void*)fn, dim3(grid), dim3(64), kargs, 0, (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
 attn_status attn_launch_combine(const attn_plan_s* plan, const attn::RunParams& p, void* stream) {
     attn::RunParams args = p;
     void* kargs[] = {&args};
+    const void* fn = plan->desc.head_dim == 128 ? (const void*)attn::combine_kernel<128>
+                                                : (const void*)attn::combine_kernel<256>;
     const unsigned grid = (unsigned)p.batch * p.num_kv_heads * ((p.rows + 3) / 4);
-    hipError_t e = hipLaunchKernel((const void*)attn::combine_kernel_d256, dim3(grid), dim3(256), kargs, 0,
-                                   (hipStream_t)stream);
-    (void)plan;
+    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(256), kargs, 0, (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 

@@ -24,19 +24,23 @@ struct Geometry {
 
 // The kernels compiled into this library.
 constexpr Geometry kGeometries[] = {
-    {ATTN_KV_E4M3, 256, 8, attn::kRowsAlloc},
+    {ATTN_KV_E4M3, 256, 8, attn::kMaxRows},
+    {ATTN_KV_FP16, 128, 8, attn::kMaxRows},
 };
 constexpr int kNumGeometries = sizeof(kGeometries) / sizeof(kGeometries[0]);
 
 bool aligned(int64_t v, int64_t a) { return v > 0 && v % a == 0; }
 
-attn::SplitPolicy policy_for(int num_cus) {
+attn::SplitPolicy policy_for(int num_cus, int num_kv_heads) {
     attn::SplitPolicy p;
-    // One split per (slot, KV head) per 8 CUs: a B8 x Hkv4 batch of long rows then puts
-    // 8*4*(num_cus/8) = 4*num_cus single-wave workgroups in flight - one per SIMD. At least 32
-    // splits, so a partition never exceeds 262144/32 = 8192 tokens (the kernel stages one
-    // split's block-table entries in LDS).
-    p.split_cap = num_cus / 8 > 32 ? num_cus / 8 : 32;
+    // Aim one single-wave workgroup at every SIMD (4 per CU) for a typical batch of 8 long
+    // rows: cap = 4 * CUs / (8 * Hkv) splits per (slot, KV head), i.e. 32 at Hkv 4 and 16 at
+    // Hkv 8 on 256 CUs. The cap depends on the device and the head geometry only - never on the
+    // batch - so a request's partitions, and its output bits, are the same alone or batched.
+    // Clamped to [16, 128]: partitions stay <= 262144 / 16 = 16384 tokens (the kernel stages a
+    // split's block-table entries in LDS) and >= 512 tokens (part_min) keep partial traffic small.
+    const int cap = num_cus * 4 / (8 * num_kv_heads);
+    p.split_cap = cap < 16 ? 16 : (cap > 128 ? 128 : cap);
     p.part_min = 512;
     p.part_align = 256;
     return p;
@@ -104,7 +108,7 @@ attn_status attn_plan(const attn_desc* d, int device, attn_plan_t* out, size_t* 
     p->desc = *d;
     p->device = device;
     p->num_cus = num_cus;
-    p->policy = policy_for(num_cus);
+    p->policy = policy_for(num_cus, d->num_kv_heads);
     int32_t gs = 0;
     for (int32_t L = 1; L <= d->max_seq_len; ++L) {
         const int32_t s = attn::num_splits(L, p->policy);
@@ -113,7 +117,8 @@ attn_status attn_plan(const attn_desc* d, int device, attn_plan_t* out, size_t* 
     p->grid_splits = gs;
     p->rows = (int32_t)rows;
     p->sm_scale = d->sm_scale > 0.0f ? d->sm_scale : (float)(1.0 / sqrt((double)d->head_dim));
-    const size_t floats = (size_t)attn::kRowsAlloc * d->head_dim + 2 * attn::kRowsAlloc;
+    p->rows_alloc = (int32_t)((rows + 15) / 16 * 16);
+    const size_t floats = (size_t)p->rows_alloc * d->head_dim + 2 * (size_t)p->rows_alloc;
     const size_t align_f = attn::kWorkspaceAlign / sizeof(float);
     p->split_floats = (floats + align_f - 1) / align_f * align_f;
     p->split_bytes = p->split_floats * sizeof(float);
@@ -210,6 +215,7 @@ attn_status attn_prepare(attn_plan_t p, const attn_args* a, void* stream, attn::
     rp->num_kv_heads = d.num_kv_heads;
     rp->group = d.num_q_heads / d.num_kv_heads;
     rp->rows = p->rows;
+    rp->rows_alloc = p->rows_alloc;
     rp->grid_splits = p->grid_splits;
     rp->causal = d.causal;
     rp->split_floats = (int32_t)p->split_floats;
