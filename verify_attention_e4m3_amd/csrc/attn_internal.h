@@ -48,6 +48,11 @@ ATTN_HD int32_t num_splits(int32_t L, SplitPolicy p) {
     return (L + P - 1) / P;
 }
 
+// 64-bit value from two 32-bit words. Both parameters are unsigned, so a low word with bit 31
+// set is never sign-extended into the high half (the wave-uniform copies of a pointer made with
+// readfirstlane come back as signed ints).
+ATTN_HD uint64_t join_words(uint32_t hi, uint32_t lo) { return ((uint64_t)hi << 32) | (uint64_t)lo; }
+
 // Kernel parameters, passed by value (a captured hipGraph keeps a copy; nothing points at
 // host memory).
 struct RunParams {

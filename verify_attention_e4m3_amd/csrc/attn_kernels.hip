@@ -67,9 +67,9 @@ __device__ __forceinline__ int32_t clamp_len(int32_t L, int32_t max_len) {
 }
 
 constexpr float kRefSlack = 10.0f;
-// Block-table entries one split can touch: partitions are at most 16384 tokens and pages hold
-// at least 16 tokens, so a split spans at most 16384/16 + 1 pages.
-constexpr int kMaxSplitPages = 16384 / 16 + 2;
+// Block-table entries one split can touch: partitions are at most 32768 tokens and pages hold
+// at least 16 tokens, so a split spans at most 32768/16 + 1 pages.
+constexpr int kMaxSplitPages = 32768 / 16 + 2;
 
 // One 32-token tile as each lane holds it (see LaneOffs for which bytes).
 struct TileK { u32x4 k[2][4]; };
@@ -227,7 +227,11 @@ __device__ __forceinline__ Granules granules(int32_t j0, int32_t last, const int
 // waiting to the explicit vmcnt waits of the tile loop. The KV cache is read exactly once, so
 // the loads carry the non-temporal (streaming) hint.
 __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(lds), "v"(voff), "s"(base)
+    const uint64_t b64 = (uint64_t)base;
+    const uint64_t sbase = join_words((uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32)),
+                                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64));
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
+                 "v"(voff), "s"(sbase)
                  : "memory", "m0");
 }
 
@@ -410,14 +414,27 @@ __device__ __forceinline__ void split_row_max(float (&m)[RT], int32_t j_begin, i
     }
 }
 
-// Split kernel: one 64-lane wave per (slot, KV head, split); RT row tiles of 16 packed rows.
+// Split kernel: a workgroup of two 64-lane waves per (slot, KV head, split); RT row tiles of
+// 16 packed rows. Wave w streams the split's tiles w, w+2, w+4, ... through its own LDS ring;
+// at the end wave 1 hands its partial state to wave 0 through LDS, and wave 0 merges the two
+// (always wave 0's first) and writes the split's panel. Two waves per split halve the number
+// of splits, and with it the partial traffic, for the same number of waves in flight.
+constexpr int kWavesPerSplit = 2;
+
+struct SplitLds {
+    __attribute__((aligned(16))) uint8_t rings[kWavesPerSplit][2 * kStageBytes];
+    int32_t pages[kMaxSplitPages];
+};
+static_assert(sizeof(SplitLds::rings) <= 65536, "direct-load LDS addresses must stay below 64 KB");
+
 template <int FMT, int RT>
-__global__ __launch_bounds__(64) void split_kernel(RunParams p) {
+__global__ __launch_bounds__(128) void split_kernel(RunParams p) {
     using F = Fmt<FMT>;
     constexpr int D = F::D;
     constexpr int KS = F::KSTEPS;
     constexpr int JT = F::JT;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform within a wave
     const int n = lane & 15;       // MFMA column = packed row within a row tile
     const int qd = lane >> 4;      // quarter of the wave
 
@@ -433,7 +450,7 @@ __global__ __launch_bounds__(64) void split_kernel(RunParams p) {
 
     const int32_t L = clamp_len(p.seq_lens[b], p.max_seq_len);
     const int32_t S = num_splits(L, p.policy);
-    if (s >= S) return;
+    if (s >= S) return;                 // uniform over the workgroup
     const int32_t P = partition_len(L, p.policy);
     const int32_t j_begin = s * P;
     const int32_t j_end = min(j_begin + P, L);
@@ -483,27 +500,29 @@ __global__ __launch_bounds__(64) void split_kernel(RunParams p) {
 
     const uint8_t* kbase = p.k + (int64_t)g * p.k_head_stride;
     const uint8_t* vbase = p.v + (int64_t)g * p.v_head_stride;
-    // The split's block-table entries, clamped into the caches, staged once in LDS: the tile
-    // loop then issues no compiler-visible global load (whose wait would also drain the ring).
-    __shared__ int32_t pages[kMaxSplitPages];
+    // LDS: the two waves' rings first (so every direct-load LDS address is below 64 KB), then the
+    // split's block-table entries, clamped into the caches and staged once: the tile loop then
+    // issues no compiler-visible global load (whose wait would also drain the ring).
+    __shared__ SplitLds lds;
+    int32_t* pages = lds.pages;
     int32_t pg0, pg_last, unused_slot;
     locate(j_begin, p, pg0, unused_slot);
     locate(last, p, pg_last, unused_slot);
     {
         const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
-        for (int i = lane; i <= pg_last - pg0; i += 64) {
+        for (int i = threadIdx.x; i <= pg_last - pg0; i += 64 * kWavesPerSplit) {
             const int32_t v = bt[pg0 + i];
             pages[i] = v < 0 ? 0 : (v >= p.num_pages ? (int32_t)(p.num_pages - 1) : v);
         }
     }
     __syncthreads();
 
-    // Two-stage LDS ring: tile i lives in stage i % 2. Tiles i+1 and i+2 are in flight while
-    // tile i is computed: tile i+2's K (V) loads are issued into stage i % 2 as soon as tile
-    // i's K (V) has been read into registers. Past the split's end the last tile is loaded
-    // again, so every iteration issues the same 16 loads and `vmcnt(16)` always means "tile i
-    // has landed".
-    __shared__ __attribute__((aligned(16))) uint8_t ring[2 * kStageBytes];
+    // Per-wave two-stage LDS ring: the wave's k-th tile lives in stage k % 2. Its tiles k+1 and
+    // k+2 are in flight while tile k is computed: tile k+2's K (V) loads are issued into stage
+    // k % 2 as soon as tile k's K (V) has been read into registers. Past the split's end the
+    // prefetches re-read one row, so every iteration issues the same 16 loads and `vmcnt(16)`
+    // always means "tile k has landed". After the tile loops the rings hold the hand-over.
+    uint8_t* ring = lds.rings[wave];
     const uint32_t ring0 = lds_addr(ring);
     const u32x4* ring_lane = reinterpret_cast<const u32x4*>(ring) + lane;
     const LaneOffs lo = lane_offsets(p, lane, n, qd);
@@ -512,14 +531,16 @@ __global__ __launch_bounds__(64) void split_kernel(RunParams p) {
     uint32_t k_rd[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) k_rd[i] = n * 256 + 16 * ((4 * i + qd) ^ n);
+    constexpr int32_t kStride = kWavesPerSplit * kTileTokens;   // tokens between a wave's tiles
+    const int32_t first = j_begin + wave * kTileTokens;          // this wave's first tile
 
     // Per-row reference max (log2 units). A row's reference is the max of the first tile in
-    // which it sees a key; exponentials are taken against it, so O and l never need
-    // rescaling and the O accumulators are touched only by MFMAs. A later tile may exceed the
-    // reference by up to kRefSlack (P <= 2^kRefSlack, exact range in FP16 and FP32). If one
-    // exceeds it by more, the split is recomputed once with each row's exact maximum over the
-    // split as its reference (then no tile can exceed it). Both passes depend only on the
-    // split's own data, so the result is deterministic.
+    // which the wave sees a key for it; exponentials are taken against it, so O and l never
+    // need rescaling and the O accumulators are touched only by MFMAs. A later tile may exceed
+    // the reference by up to kRefSlack (P <= 2^kRefSlack, exact range in FP16 and FP32). If one
+    // exceeds it by more, the wave recomputes its tiles once with each row's exact maximum
+    // over the split as its reference (then no tile can exceed it). Both passes depend only on
+    // the split's own data, so the result is deterministic.
     float m_ref[RT];
     float l_run[RT];
     float4v o[RT][JT];
@@ -531,20 +552,21 @@ __global__ __launch_bounds__(64) void split_kernel(RunParams p) {
 #pragma unroll
             for (int j = 0; j < JT; ++j) o[rt][j] = float4v{0.f, 0.f, 0.f, 0.f};
         }
+        if (first > last) return false;          // a short split may leave wave 1 no tile
         {
-            const Granules g0 = granules(j_begin, last, pages, pg0, kbase, vbase, p);
+            const Granules g0 = granules(first, last, pages, pg0, kbase, vbase, p);
             issue_k(g0, last, lo, ring0, p, lane);
             issue_v(g0, last, lo, ring0, p, n, qd);
-            const Granules g1 = granules(j_begin + kTileTokens, last, pages, pg0, kbase, vbase, p);
+            const Granules g1 = granules(first + kStride, last, pages, pg0, kbase, vbase, p);
             issue_k(g1, last, lo, ring0 + kStageBytes, p, lane);
             issue_v(g1, last, lo, ring0 + kStageBytes, p, n, qd);
         }
         bool over = false;
-        int32_t j0 = j_begin;
+        int32_t j0 = first;
         for (int st = 0;; st ^= 1) {
             const uint32_t stage = ring0 + st * kStageBytes;
             const u32x4* sl = ring_lane + st * (kStageBytes / 16);
-            const Granules gn = granules(j0 + 2 * kTileTokens, last, pages, pg0, kbase, vbase, p);
+            const Granules gn = granules(j0 + 2 * kStride, last, pages, pg0, kbase, vbase, p);
             vm_wait_tile();
             TileK tk;
             const uint8_t* stage_bytes = ring + st * kStageBytes;
@@ -566,46 +588,73 @@ __global__ __launch_bounds__(64) void split_kernel(RunParams p) {
             issue_v(gn, last, lo, stage, p, n, qd);
             if (over) break;
             F::template pv<RT>(tv, pop, o);
-            j0 += kTileTokens;
+            j0 += kStride;
             if (j0 > last) break;
         }
         vm_wait_all();   // no load may still be writing the ring when the wave moves on
         return over;
     };
 
-    const int rows_alloc = 16 * RT;
-    float* panel = p.ws + ((int64_t)(b * p.num_kv_heads + g) * p.grid_splits + s) * p.split_floats;
-    // Split epilogue: O^T tile j holds O[row n][dim F::o_dim(qd, i, j)] in element i; for a fixed
-    // i, groups of 4 consecutive j are 4 consecutive dims.
-    auto store_panel = [&]() {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const int r = rt * 16 + n;
-            float* orow = panel + r * D;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int c4 = 0; c4 < JT / 4; ++c4)
-                    *reinterpret_cast<float4v*>(orow + F::o_dim(qd, i, 4 * c4)) =
-                        float4v{o[rt][4 * c4][i], o[rt][4 * c4 + 1][i], o[rt][4 * c4 + 2][i], o[rt][4 * c4 + 3][i]};
-            float l = l_run[rt];
-            l += __shfl_xor(l, 16);
-            l += __shfl_xor(l, 32);
-            if (qd == 0) {
-                panel[rows_alloc * D + r] = m_ref[rt];
-                panel[rows_alloc * D + rows_alloc + r] = l;
-            }
-        }
-    };
-
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) m_ref[rt] = -INFINITY;
-    const bool over = run_pass();
-    store_panel();
-    if (over) {
+    if (run_pass()) {
         split_row_max<FMT, RT>(m_ref, j_begin, j_end, mask_from, lim, c, pages, pg0, kbase, vbase, p, qop, n, qd);
         run_pass();
-        store_panel();
+    }
+
+    // Hand-over: wave 1 writes its accumulators (element i of O^T tile (rt, j) as row
+    // (rt*JT + j)*4 + i of 64 lanes), its references and its lane-partial sums into the rings;
+    // wave 0 reads the same lane's values back, so both sides are conflict-free.
+    __syncthreads();                         // both waves are done with their rings
+    float* xfer = reinterpret_cast<float*>(&lds.rings[0][0]);
+    if (wave == 1) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+            for (int j = 0; j < JT; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xfer[((rt * JT + j) * 4 + i) * 64 + lane] = o[rt][j][i];
+            xfer[(RT * JT * 4 + rt) * 64 + lane] = m_ref[rt];
+            xfer[(RT * JT * 4 + RT + rt) * 64 + lane] = l_run[rt];
+        }
+    }
+    __syncthreads();
+    if (wave == 1) return;
+
+    // Merge (wave 0 first, then wave 1) and write the split's panel: O^T tile j holds
+    // O[row n][dim F::o_dim(qd, i, j)] in element i; for a fixed i, groups of 4 consecutive j
+    // are 4 consecutive dims.
+    const int rows_alloc = 16 * RT;
+    float* panel = p.ws + ((int64_t)(b * p.num_kv_heads + g) * p.grid_splits + s) * p.split_floats;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const float m1 = xfer[(RT * JT * 4 + rt) * 64 + lane];
+        const float l1 = xfer[(RT * JT * 4 + RT + rt) * 64 + lane];
+        const float m0 = m_ref[rt];
+        const float M = fmaxf(m0, m1);
+        const float a0 = m0 == -INFINITY ? 0.0f : fast_exp2(m0 - M);
+        const float a1 = m1 == -INFINITY ? 0.0f : fast_exp2(m1 - M);
+        const int r = rt * 16 + n;
+        float* orow = panel + r * D;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c4 = 0; c4 < JT / 4; ++c4) {
+                float4v v;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int j = 4 * c4 + u;
+                    v[u] = a0 * o[rt][j][i] + a1 * xfer[((rt * JT + j) * 4 + i) * 64 + lane];
+                }
+                *reinterpret_cast<float4v*>(orow + F::o_dim(qd, i, 4 * c4)) = v;
+            }
+        float l = a0 * l_run[rt] + a1 * l1;
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        if (qd == 0) {
+            panel[rows_alloc * D + r] = M;
+            panel[rows_alloc * D + rows_alloc + r] = l;
+        }
     }
 }
 
@@ -704,7 +753,8 @@ attn_status attn_launch_split(const attn_plan_s* plan, const attn::RunParams& p,
     attn::KernelFn fn = plan->desc.kv_dtype == ATTN_KV_FP16 ? attn::split_for_rows<attn::kFmtF16D128>(row_tiles)
                                                              : attn::split_for_rows<attn::kFmtE4M3D256>(row_tiles);
     const unsigned grid = (unsigned)p.batch * p.num_kv_heads * p.grid_splits;
-    hipError_t e = hipLaunchKernel((const void*)fn, dim3(grid), dim3(64), kargs, 0, (hipStream_t)stream);
+    hipError_t e = hipLaunchKernel((const void*)fn, dim3(grid), dim3(64 * attn::kWavesPerSplit), kargs, 0,
+                                   (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 

@@ -9,6 +9,7 @@
 // single-request optimization was missing from concurrent decode"; SM70 coverage page,
 // section "Compiled-library precision admission").
 #include <math.h>
+#include <stdint.h>
 #include <new>
 #include <string.h>
 
@@ -33,14 +34,14 @@ bool aligned(int64_t v, int64_t a) { return v > 0 && v % a == 0; }
 
 attn::SplitPolicy policy_for(int num_cus, int num_kv_heads) {
     attn::SplitPolicy p;
-    // Aim one single-wave workgroup at every SIMD (4 per CU) for a typical batch of 8 long
-    // rows: cap = 4 * CUs / (8 * Hkv) splits per (slot, KV head), i.e. 32 at Hkv 4 and 16 at
-    // Hkv 8 on 256 CUs. The cap depends on the device and the head geometry only - never on the
-    // batch - so a request's partitions, and its output bits, are the same alone or batched.
-    // Clamped to [16, 128]: partitions stay <= 262144 / 16 = 16384 tokens (the kernel stages a
-    // split's block-table entries in LDS) and >= 512 tokens (part_min) keep partial traffic small.
-    const int cap = num_cus * 4 / (8 * num_kv_heads);
-    p.split_cap = cap < 16 ? 16 : (cap > 128 ? 128 : cap);
+    // Aim one wave at every SIMD (4 per CU, two per split) for a typical batch of 8 long rows:
+    // cap = 2 * CUs / (8 * Hkv) splits per (slot, KV head), i.e. 16 at Hkv 4 and 8 at Hkv 8 on
+    // 256 CUs. The cap depends on the device and the head geometry only - never on the batch -
+    // so a request's partitions, and its output bits, are the same alone or batched. Clamped to
+    // [8, 64]: partitions stay <= 262144 / 8 = 32768 tokens (the kernel stages a split's
+    // block-table entries in LDS) and >= 512 tokens (part_min) keep partial traffic small.
+    const int cap = num_cus * 2 / (8 * num_kv_heads);
+    p.split_cap = cap < 8 ? 8 : (cap > 64 ? 64 : cap);
     p.part_min = 512;
     p.part_align = 256;
     return p;
@@ -84,6 +85,8 @@ attn_status attn_plan(const attn_desc* d, int device, attn_plan_t* out, size_t* 
                                 d->v_page_stride, d->v_token_stride, d->v_head_stride};
     for (int64_t s : strides)
         if (!aligned(s, attn::kStrideAlign)) return ATTN_E_INVALID;
+    // The kernel addresses a 16-token granule with 32-bit lane offsets from its first token.
+    if (16 * d->k_token_stride + 4096 > INT32_MAX || 16 * d->v_token_stride + 4096 > INT32_MAX) return ATTN_E_INVALID;
     if (!(d->sm_scale >= 0.0f) || isinf(d->sm_scale)) return ATTN_E_INVALID;   // also rejects NaN
     if (d->causal != 0 && d->causal != 1) return ATTN_E_INVALID;
 
