@@ -25,7 +25,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "verify_b8_ctx128k_gqa6_16layers"
 METRIC = "KV read GB/s (% of 8 TB/s HBM) + attention ms/layer, B8 q8 D256 GQA6 128K ctx"
-COUNTERS = os.path.join(ROOT, "profiles", "split_kernel_e4m3_d256_b8_ctx128k_counters.json")
+
+
+def counters_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"split_kernel_{workload}_counters.json")
 
 
 def kernel_source_hash() -> str:
@@ -36,36 +39,40 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(units_per_launch: int):
+def measured_traffic(workload: str, units_per_launch: int):
     """HBM bytes per split-kernel launch from committed rocprofv3 counters, if they were taken on
     the current kernel source; otherwise None."""
-    if not os.path.exists(COUNTERS):
+    path = counters_path(workload)
+    if not os.path.exists(path):
         return None
-    with open(COUNTERS) as f:
+    with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_source_sha256") != kernel_source_hash():
         return None
     return int(rec["hbm_bytes_per_dispatch"])
 
 
-def stream_read_probe(torch, dev, nbytes: int, reps: int = 10) -> float:
-    """GB/s of a plain streaming-read kernel (libattn_probe.so) over nbytes of device memory."""
+def stream_read_probe(torch, dev, nbytes: int, lds: bool, reps: int = 10) -> float:
+    """GB/s of a streaming-read probe (libattn_probe.so) over about nbytes of device memory: the
+    register-load form, or the LDS-DMA form the split kernel uses (lds=True)."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "verify_attention_e4m3_amd", "libattn_probe.so"))
-    lib.attn_probe_stream_read.restype = ctypes.c_int
-    lib.attn_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
-                                           ctypes.c_void_p]
-    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    fn = lib.attn_probe_stream_read_lds if lds else lib.attn_probe_stream_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     grid = 2048
+    if lds:                                  # whole 16 KB stages per wave
+        nbytes -= nbytes % (grid * 16384)
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     sink = torch.empty(grid * 4, dtype=torch.int32, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    if lib.attn_probe_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), grid, stream) != 0:
+    if fn(src.data_ptr(), nbytes, sink.data_ptr(), grid, stream) != 0:
         raise RuntimeError("stream probe launch failed")
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
     for _ in range(reps):
-        lib.attn_probe_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), grid, stream)
+        fn(src.data_ptr(), nbytes, sink.data_ptr(), grid, stream)
     e.record()
     torch.cuda.synchronize()
     return nbytes * reps / (s.elapsed_time(e) * 1e-3) / 1e9
@@ -135,6 +142,8 @@ def main():
     lens = [int(x) for x in c0["seq_lens"].cpu().tolist()]
     kv_bytes = wl.kv_bytes(lens, w.num_kv_heads, w.head_dim, elem)
     token_heads = sum(lens) * w.num_kv_heads
+    # split_kernel<format, row tiles>: format 0 = E4M3 D256, 1 = FP16 D128; 16 packed rows per tile
+    kernel_name = f"split_kernel<{0 if w.kv_format == 'e4m3' else 1}, {-(-plan.info['rows'] // 16)}>"
 
     def step(i):
         a = arglist[i % w.layers]
@@ -209,8 +218,9 @@ def main():
     torch.cuda.synchronize()
     copy_gbs = 2 * probe_src.numel() * 10 / (s.elapsed_time(e) * 1e-3) / 1e9
     del probe_src, probe_dst
-    read_gbs = stream_read_probe(torch, dev, kv_bytes)
-    traffic = measured_traffic(token_heads)
+    read_gbs = stream_read_probe(torch, dev, kv_bytes, lds=False)
+    dma_gbs = stream_read_probe(torch, dev, kv_bytes, lds=True)
+    traffic = measured_traffic(w.name, token_heads)
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
@@ -222,13 +232,14 @@ def main():
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "split_kernel_e4m3_d256", "split_ms_mean": round(split_ms_mean, 5),
+                     "kernel": kernel_name, "split_ms_mean": round(split_ms_mean, 5),
                      "algorithmic_bytes_per_launch": kv_bytes, "units_per_launch": token_heads,
                      "bytes_per_unit": 2 * w.head_dim * elem},
         "graph_replay": graph,
         "copy_probe_gbs": round(copy_gbs, 1),
         "read_probe_gbs": round(read_gbs, 1),
-        "split_frac_of_read_probe": round(achieved / read_gbs, 4),
+        "lds_dma_read_probe_gbs": round(dma_gbs, 1),
+        "split_frac_of_lds_dma_probe": round(achieved / dma_gbs, 4),
         "split_ms_p10_p50_p90": [round(x, 5) for x in statistics.quantiles(split_ms, n=10)[0::4]],
     }
     if not args.no_cpu_baseline:

@@ -658,13 +658,15 @@ __global__ __launch_bounds__(128) void split_kernel(RunParams p) {
     }
 }
 
-// Log-sum-exp combine: one wave per packed row. Lane s holds split s's (m, l) (splits past 64
-// are folded in by lane s % 64 in order), the max and the denominator are wave reductions, and
-// the O sum visits the splits in index order with every lane covering D/64 dims; the split
-// order is fixed, so the FP32 sums are bitwise reproducible.
+// Log-sum-exp combine: one wave per packed row. Lane s loads split s's (m, l) while every lane
+// already loads its D/64 dims of the first 16 splits' O, so the row costs about one memory
+// round trip; the max and the denominator are wave reductions in a fixed tree, each split's
+// weight is broadcast from the lane that owns it, and O is summed in split order - the FP32
+// sums are bitwise reproducible.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(RunParams p) {
     constexpr int VW = D / 64;
+    constexpr int kChunk = 16;
     typedef float floatv __attribute__((ext_vector_type(VW)));
     typedef _Float16 halfv __attribute__((ext_vector_type(VW)));
     const int lane = threadIdx.x & 63;
@@ -681,47 +683,41 @@ __global__ __launch_bounds__(256) void combine_kernel(RunParams p) {
     const int h = g * p.group + (r - t * p.group);
 
     const int32_t L = clamp_len(p.seq_lens[b], p.max_seq_len);
-    const int32_t S = num_splits(L, p.policy);
+    const int32_t S = num_splits(L, p.policy);          // <= 64 splits per (slot, KV head)
     const float* panel0 = p.ws + (int64_t)(b * p.num_kv_heads + g) * p.grid_splits * p.split_floats;
     const int64_t m_off = (int64_t)p.rows_alloc * D + r;
     const int64_t l_off = m_off + p.rows_alloc;
+    const float* orow = panel0 + r * D + VW * lane;
 
-    float mloc = -INFINITY;
-    for (int s = lane; s < S; s += 64) mloc = fmaxf(mloc, panel0[(int64_t)s * p.split_floats + m_off]);
+    // Split indices past S read split S-1's panel (written by this run, so finite) and get
+    // weight 0 from their lane, so the sums need no per-split branches.
+    const int32_t s_last = S > 0 ? S - 1 : 0;
+    floatv ov[kChunk];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
-    const float M = mloc;
+    for (int u = 0; u < kChunk; ++u)
+        ov[u] = *reinterpret_cast<const floatv*>(orow + (int64_t)min(u, s_last) * p.split_floats);
+    const float ms = lane < S ? panel0[(int64_t)lane * p.split_floats + m_off] : -INFINITY;
+    const float ls = lane < S ? panel0[(int64_t)lane * p.split_floats + l_off] : 0.0f;
 
+    float M = ms;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     floatv acc = {};
     float den = 0.0f;
     if (M != -INFINITY) {
-        float dloc = 0.0f;
-        for (int s = lane; s < S; s += 64) {
-            const float ms = panel0[(int64_t)s * p.split_floats + m_off];
-            const float w = ms == -INFINITY ? 0.0f : fast_exp2(ms - M);
-            dloc += w * panel0[(int64_t)s * p.split_floats + l_off];
-        }
+        const float w = ms == -INFINITY ? 0.0f : fast_exp2(ms - M);
+        den = w * ls;
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) dloc += __shfl_xor(dloc, off);
-        den = dloc;
-        const float* orow = panel0 + r * D + VW * lane;
-        int s = 0;
-        for (; s + 4 <= S; s += 4) {
-            floatv ov[4];
-            float w[4];
+        for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
+        for (int s0 = 0; s0 < S; s0 += kChunk) {
+            if (s0 > 0) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                ov[u] = *reinterpret_cast<const floatv*>(orow + (int64_t)(s + u) * p.split_floats);
-                const float ms = panel0[(int64_t)(s + u) * p.split_floats + m_off];
-                w[u] = ms == -INFINITY ? 0.0f : fast_exp2(ms - M);
+                for (int u = 0; u < kChunk; ++u)
+                    ov[u] = *reinterpret_cast<const floatv*>(orow + (int64_t)min(s0 + u, s_last) * p.split_floats);
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) acc += w[u] * ov[u];
-        }
-        for (; s < S; ++s) {
-            const floatv ov = *reinterpret_cast<const floatv*>(orow + (int64_t)s * p.split_floats);
-            const float ms = panel0[(int64_t)s * p.split_floats + m_off];
-            acc += (ms == -INFINITY ? 0.0f : fast_exp2(ms - M)) * ov;
+            for (int u = 0; u < kChunk; ++u)      // lane s0+u < 64 holds split s0+u's weight (0 past S)
+                acc += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), s0 + u)) * ov[u];
         }
     }
     const float scale = den > 0.0f ? (*p.v_scale) / den : 0.0f;
