@@ -111,8 +111,10 @@ def cpu_baseline(w, case, budget_s: float = 15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=64)
-    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--steps", type=int, default=128)
+    # The GPU needs about 40 ms of this load before its clocks settle: with 16 warmup steps the
+    # timed region still runs about 6% slow.
+    ap.add_argument("--warmup", type=int, default=128)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
@@ -129,6 +131,10 @@ def main():
     w = wl.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    # All work goes to a stream of its own, as in a serving loop: torch's default stream is
+    # HIP's null stream, whose implicit synchronisation with other streams costs several µs
+    # per launch.
+    torch.cuda.set_stream(torch.cuda.Stream(dev))
     layers = [wl.workload_case(w, device=dev, layer=i) for i in range(w.layers)]
     c0 = layers[0]
     plan = A.Plan(q_len=w.q_len, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
@@ -154,7 +160,7 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region: exactly K steps (split + combine per step), eager on the current stream,
+    # Timed region: exactly K steps (split + combine per step), eager on the work stream,
     # bracketed by device synchronisation. Nothing else is enqueued in between.
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()

@@ -78,6 +78,27 @@ def test_parity_distinct_k_and_v_scales():
     compare(run_gpu(c), run_oracle(c))
 
 
+def test_power_of_two_scales_are_exact():
+    # Scaling by powers of two commutes with FP32/FP16 rounding (no overflow at these values):
+    # (2Q, k_scale) and (Q, 2 k_scale) give the same bits, and doubling v_scale doubles every
+    # output whose FP16 value stays normal (subnormals round on a fixed grid).
+    note("power-of-two scale metamorphics, B2 L900/5000 Hq12 Hkv2")
+    c = _case(batch=2, seq_lens=[900, 5000], q_len=8, num_q_heads=12, num_kv_heads=2, head_dim=256, page_size=32,
+              seed=9)
+    base = run_gpu(c).clone()
+    c2 = dict(c)
+    c2["q"] = c["q"] * 2
+    c2["k_scale"] = c["k_scale"] * 0.5
+    assert torch.equal(run_gpu(c2).view(torch.int16), base.view(torch.int16))
+    c3 = dict(c)
+    c3["v_scale"] = c["v_scale"] * 2
+    doubled = run_gpu(c3)
+    big = base.abs() >= 2.0 ** -13
+    assert big.float().mean() > 0.9
+    assert torch.equal(doubled[big].view(torch.int16), (base[big] * 2).view(torch.int16))
+    assert ((doubled[~big].float() - 2 * base[~big].float()).abs() <= 2.0 ** -24).all()
+
+
 FP16_D128 = [
     dict(batch=2, seq_lens=[1, 3000], q_len=1, num_q_heads=8, num_kv_heads=2, page_size=16),
     dict(batch=3, seq_lens=[40, 1649, 7], q_len=1, num_q_heads=32, num_kv_heads=8, page_size=1648),
@@ -122,6 +143,23 @@ def test_batched_equals_single_bitwise():
               page_size=1648, seed=9, max_seq_len=65536)
     batched = run_gpu(c, batch_capacity=16)
     for b in range(5):
+        one = {k: (v[b:b + 1] if k in ("q", "block_table", "seq_lens") else v) for k, v in c.items()}
+        single = run_gpu(one, batch_capacity=1)
+        assert torch.equal(single[0].view(torch.int16), batched[b].view(torch.int16)), b
+
+
+def test_paired_head_workgroups_equal_single_bitwise():
+    # B8 at Hkv4 and 64K fills the chip with workgroups that hold two KV heads each; one slot
+    # alone runs one head per workgroup. Both run each head's split the same way.
+    note("head-pair workgroups vs single-slot runs, B8 Hkv4 max 65536")
+    lens = [3297, 0, 40000, 8, 131, 65536, 1, 20000]
+    c = _case(batch=8, seq_lens=lens, q_len=8, num_q_heads=24, num_kv_heads=4, head_dim=256, page_size=1648,
+              seed=19, max_seq_len=65536)
+    plan = plan_for(c)
+    gs = plan.info["grid_splits"]
+    assert 8 * 2 * gs >= plan.info["num_cus"] > 2 * gs       # batched pairs heads, single does not
+    batched = run_gpu(c, plan)
+    for b in range(8):
         one = {k: (v[b:b + 1] if k in ("q", "block_table", "seq_lens") else v) for k, v in c.items()}
         single = run_gpu(one, batch_capacity=1)
         assert torch.equal(single[0].view(torch.int16), batched[b].view(torch.int16)), b

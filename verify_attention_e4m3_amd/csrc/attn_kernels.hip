@@ -414,37 +414,45 @@ __device__ __forceinline__ void split_row_max(float (&m)[RT], int32_t j_begin, i
     }
 }
 
-// Split kernel: a workgroup of two 64-lane waves per (slot, KV head, split); RT row tiles of
-// 16 packed rows. Wave w streams the split's tiles w, w+2, w+4, ... through its own LDS ring;
-// at the end wave 1 hands its partial state to wave 0 through LDS, and wave 0 merges the two
-// (always wave 0's first) and writes the split's panel. Two waves per split halve the number
-// of splits, and with it the partial traffic, for the same number of waves in flight.
-constexpr int kWavesPerSplit = 2;
+// Split kernel: a workgroup holds HP KV heads of one (slot, split), two 64-lane waves per head;
+// RT row tiles of 16 packed rows. Wave w serves head HP*pair + w % HP and streams that head's
+// tiles w / HP, w / HP + 2, ... of the split through its own LDS ring; at the end the second
+// wave of each head hands its partial state to the first through LDS, which merges the two
+// (always its own first) and writes the head's split panel. Two waves per split halve the
+// number of splits, and with it the partial traffic, for the same number of waves in flight.
+// With HP = 2 (even head counts) the waves of a workgroup read neighbouring head rows of the
+// same tokens, so one CU streams whole 2*D-byte runs of each token row instead of isolated
+// D-byte pieces; on MI355X that raises the sustained read rate of the paged stream by about a
+// tenth over one head per workgroup.
+constexpr int kWavesPerHead = 2;
 
+template <int HP>
 struct SplitLds {
-    __attribute__((aligned(16))) uint8_t rings[kWavesPerSplit][2 * kStageBytes];
+    __attribute__((aligned(16))) uint8_t rings[kWavesPerHead * HP][2 * kStageBytes];
     int32_t pages[kMaxSplitPages];
 };
-static_assert(sizeof(SplitLds::rings) <= 65536, "direct-load LDS addresses must stay below 64 KB");
 
-template <int FMT, int RT>
-__global__ __launch_bounds__(128) void split_kernel(RunParams p) {
+template <int FMT, int RT, int HP>
+__global__ __launch_bounds__(64 * kWavesPerHead * HP) void split_kernel(RunParams p) {
     using F = Fmt<FMT>;
     constexpr int D = F::D;
     constexpr int KS = F::KSTEPS;
     constexpr int JT = F::JT;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform within a wave
+    const int hl = wave % HP;      // head within the workgroup
+    const int half = wave / HP;    // which of the head's two waves
     const int n = lane & 15;       // MFMA column = packed row within a row tile
     const int qd = lane >> 4;      // quarter of the wave
 
-    // Workgroup order: KV head fastest, then split, then slot. The KV heads of one token are
-    // adjacent in the cache (token stride = Hkv * head stride), so the workgroups that read the
-    // same tokens' rows are dispatched together and stream through the same DRAM pages at
+    // Workgroup order: KV-head group fastest, then split, then slot. The KV heads of one token
+    // are adjacent in the cache (token stride = Hkv * head stride), so the workgroups that read
+    // the same tokens' rows are dispatched together and stream through the same DRAM pages at
     // about the same time.
     int wg = blockIdx.x;
-    const int g = wg % p.num_kv_heads;
-    wg /= p.num_kv_heads;
+    const int head_groups = p.num_kv_heads / HP;
+    const int g = (wg % head_groups) * HP + hl;
+    wg /= head_groups;
     const int s = wg % p.grid_splits;
     const int b = wg / p.grid_splits;
 
@@ -500,17 +508,17 @@ __global__ __launch_bounds__(128) void split_kernel(RunParams p) {
 
     const uint8_t* kbase = p.k + (int64_t)g * p.k_head_stride;
     const uint8_t* vbase = p.v + (int64_t)g * p.v_head_stride;
-    // LDS: the two waves' rings first (so every direct-load LDS address is below 64 KB), then the
-    // split's block-table entries, clamped into the caches and staged once: the tile loop then
-    // issues no compiler-visible global load (whose wait would also drain the ring).
-    __shared__ SplitLds lds;
+    // LDS: the waves' rings, then the split's block-table entries (shared by the workgroup's
+    // heads), clamped into the caches and staged once: the tile loop then issues no
+    // compiler-visible global load (whose wait would also drain the ring).
+    __shared__ SplitLds<HP> lds;
     int32_t* pages = lds.pages;
     int32_t pg0, pg_last, unused_slot;
     locate(j_begin, p, pg0, unused_slot);
     locate(last, p, pg_last, unused_slot);
     {
         const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
-        for (int i = threadIdx.x; i <= pg_last - pg0; i += 64 * kWavesPerSplit) {
+        for (int i = threadIdx.x; i <= pg_last - pg0; i += 64 * kWavesPerHead * HP) {
             const int32_t v = bt[pg0 + i];
             pages[i] = v < 0 ? 0 : (v >= p.num_pages ? (int32_t)(p.num_pages - 1) : v);
         }
@@ -531,8 +539,8 @@ __global__ __launch_bounds__(128) void split_kernel(RunParams p) {
     uint32_t k_rd[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) k_rd[i] = n * 256 + 16 * ((4 * i + qd) ^ n);
-    constexpr int32_t kStride = kWavesPerSplit * kTileTokens;   // tokens between a wave's tiles
-    const int32_t first = j_begin + wave * kTileTokens;          // this wave's first tile
+    constexpr int32_t kStride = kWavesPerHead * kTileTokens;    // tokens between a wave's tiles
+    const int32_t first = j_begin + half * kTileTokens;          // this wave's first tile
 
     // Per-row reference max (log2 units). A row's reference is the max of the first tile in
     // which the wave sees a key for it; exponentials are taken against it, so O and l never
@@ -552,7 +560,7 @@ __global__ __launch_bounds__(128) void split_kernel(RunParams p) {
 #pragma unroll
             for (int j = 0; j < JT; ++j) o[rt][j] = float4v{0.f, 0.f, 0.f, 0.f};
         }
-        if (first > last) return false;          // a short split may leave wave 1 no tile
+        if (first > last) return false;          // a short split may leave a second wave no tile
         {
             const Granules g0 = granules(first, last, pages, pg0, kbase, vbase, p);
             issue_k(g0, last, lo, ring0, p, lane);
@@ -602,12 +610,15 @@ __global__ __launch_bounds__(128) void split_kernel(RunParams p) {
         run_pass();
     }
 
-    // Hand-over: wave 1 writes its accumulators (element i of O^T tile (rt, j) as row
-    // (rt*JT + j)*4 + i of 64 lanes), its references and its lane-partial sums into the rings;
-    // wave 0 reads the same lane's values back, so both sides are conflict-free.
-    __syncthreads();                         // both waves are done with their rings
-    float* xfer = reinterpret_cast<float*>(&lds.rings[0][0]);
-    if (wave == 1) {
+    // Hand-over: each head's second wave writes its accumulators (element i of O^T tile (rt, j)
+    // as row (rt*JT + j)*4 + i of 64 lanes), its references and its lane-partial sums into the
+    // head's region of the rings; the first wave reads the same lane's values back, so both
+    // sides are conflict-free.
+    constexpr int kXferFloats = (RT * JT * 4 + 2 * RT) * 64;
+    static_assert(HP * kXferFloats * 4 <= sizeof(lds.rings), "hand-over must fit in the rings");
+    __syncthreads();                         // every wave is done with its ring
+    float* xfer = reinterpret_cast<float*>(&lds.rings[0][0]) + hl * kXferFloats;
+    if (half == 1) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
@@ -619,9 +630,9 @@ __global__ __launch_bounds__(128) void split_kernel(RunParams p) {
         }
     }
     __syncthreads();
-    if (wave == 1) return;
+    if (half == 1) return;
 
-    // Merge (wave 0 first, then wave 1) and write the split's panel: O^T tile j holds
+    // Merge (first wave, then second) and write the head's split panel: O^T tile j holds
     // O[row n][dim F::o_dim(qd, i, j)] in element i; for a fixed i, groups of 4 consecutive j
     // are 4 consecutive dims.
     const int rows_alloc = 16 * RT;
@@ -730,13 +741,27 @@ __global__ __launch_bounds__(256) void combine_kernel(RunParams p) {
 
 typedef void (*KernelFn)(RunParams);
 
-template <int FMT>
+template <int FMT, int HP>
 KernelFn split_for_rows(int row_tiles) {
     switch (row_tiles) {
-        case 1: return split_kernel<FMT, 1>;
-        case 2: return split_kernel<FMT, 2>;
-        default: return split_kernel<FMT, 3>;
+        case 1: return split_kernel<FMT, 1, HP>;
+        case 2: return split_kernel<FMT, 2, HP>;
+        default: return split_kernel<FMT, 3, HP>;
     }
+}
+
+// KV heads per split workgroup: pairs when the head count is even and the paired grid still
+// gives every CU a workgroup (a paired workgroup takes a whole CU's LDS); otherwise one head per
+// workgroup, two of which share a CU. Each head's split runs the same waves, tiles and merge
+// either way, so the choice never changes a bit of the result.
+inline int heads_per_workgroup(int num_kv_heads, int batch, int grid_splits, int num_cus) {
+    if (num_kv_heads % 2 != 0) return 1;
+    return (int64_t)batch * (num_kv_heads / 2) * grid_splits >= num_cus ? 2 : 1;
+}
+
+template <int FMT>
+KernelFn split_for(int row_tiles, int hp) {
+    return hp == 2 ? split_for_rows<FMT, 2>(row_tiles) : split_for_rows<FMT, 1>(row_tiles);
 }
 
 }  // namespace
@@ -746,10 +771,12 @@ attn_status attn_launch_split(const attn_plan_s* plan, const attn::RunParams& p,
     attn::RunParams args = p;
     void* kargs[] = {&args};
     const int row_tiles = p.rows_alloc / 16;
-    attn::KernelFn fn = plan->desc.kv_dtype == ATTN_KV_FP16 ? attn::split_for_rows<attn::kFmtF16D128>(row_tiles)
-                                                             : attn::split_for_rows<attn::kFmtE4M3D256>(row_tiles);
-    const unsigned grid = (unsigned)p.batch * p.num_kv_heads * p.grid_splits;
-    hipError_t e = hipLaunchKernel((const void*)fn, dim3(grid), dim3(64 * attn::kWavesPerSplit), kargs, 0,
+    const int hp = attn::heads_per_workgroup(p.num_kv_heads, p.batch, p.grid_splits, plan->num_cus);
+    attn::KernelFn fn = plan->desc.kv_dtype == ATTN_KV_FP16 ? attn::split_for<attn::kFmtF16D128>(row_tiles, hp)
+                                                             : attn::split_for<attn::kFmtE4M3D256>(row_tiles, hp);
+    // One workgroup per (slot, split, group of hp KV heads); the kernel decodes the same order.
+    const unsigned grid = (unsigned)p.batch * (p.num_kv_heads / hp) * p.grid_splits;
+    hipError_t e = hipLaunchKernel((const void*)fn, dim3(grid), dim3(64 * attn::kWavesPerHead * hp), kargs, 0,
                                    (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
