@@ -293,7 +293,9 @@ __device__ __forceinline__ void issue_v(const Granules& gr, int32_t last, const 
     }
 }
 
-__device__ __forceinline__ void vm_wait_tile() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
+// Every tile is 8 K loads then (later) 8 V loads, and a wave keeps two tiles in flight: when
+// tile k's K (or V) is needed, the 24 newer loads of the ring may still be outstanding.
+__device__ __forceinline__ void vm_wait_oldest_half_tile() { asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); }
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
@@ -528,8 +530,9 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void split_kernel(RunParam
     // Per-wave two-stage LDS ring: the wave's k-th tile lives in stage k % 2. Its tiles k+1 and
     // k+2 are in flight while tile k is computed: tile k+2's K (V) loads are issued into stage
     // k % 2 as soon as tile k's K (V) has been read into registers. Past the split's end the
-    // prefetches re-read one row, so every iteration issues the same 16 loads and `vmcnt(16)`
-    // always means "tile k has landed". After the tile loops the rings hold the hand-over.
+    // prefetches re-read one row, so every iteration issues the same 8 + 8 loads and `vmcnt(24)`
+    // before reading tile k's K (and again before its V) means "that half of tile k has landed":
+    // V gets until after the softmax to arrive. After the tile loops the rings hold the hand-over.
     uint8_t* ring = lds.rings[wave];
     const uint32_t ring0 = lds_addr(ring);
     const u32x4* ring_lane = reinterpret_cast<const u32x4*>(ring) + lane;
@@ -575,7 +578,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void split_kernel(RunParam
             const uint32_t stage = ring0 + st * kStageBytes;
             const u32x4* sl = ring_lane + st * (kStageBytes / 16);
             const Granules gn = granules(j0 + 2 * kStride, last, pages, pg0, kbase, vbase, p);
-            vm_wait_tile();
+            vm_wait_oldest_half_tile();         // tile k's K has landed
             TileK tk;
             const uint8_t* stage_bytes = ring + st * kStageBytes;
 #pragma unroll
@@ -590,6 +593,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void split_kernel(RunParam
             half8 pop[RT];
             over = softmax_tile<RT>(sacc, j0, mask_from, lim, c, m_ref, l_run, pop, qd);
             TileV tv;
+            vm_wait_oldest_half_tile();         // tile k's V has landed
 #pragma unroll
             for (int e = 0; e < 8; ++e) tv.v[e] = sl[(8 + e) * 64];
             lds_wait_all();
