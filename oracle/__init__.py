@@ -21,6 +21,8 @@ What it computes follows these pages:
 Parity status of each function is stated in its module header.
 """
 from .e4m3 import decode_byte, decode_table
+from .e5m2 import decode_byte as decode_e5m2_byte, decode_table as decode_e5m2_table
 from .attention import verify_attention, partial_states, merge_partials
 
-__all__ = ["decode_byte", "decode_table", "verify_attention", "partial_states", "merge_partials"]
+__all__ = ["decode_byte", "decode_table", "decode_e5m2_byte", "decode_e5m2_table", "verify_attention",
+           "partial_states", "merge_partials"]

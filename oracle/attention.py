@@ -38,8 +38,10 @@ import math
 import numpy as np
 
 from .e4m3 import decode_table
+from .e5m2 import decode_table as decode_e5m2_table
 
 _E4M3 = decode_table()
+_E5M2 = decode_e5m2_table()
 
 
 def _values(raw: np.ndarray, kv_format: str) -> np.ndarray:
@@ -48,6 +50,10 @@ def _values(raw: np.ndarray, kv_format: str) -> np.ndarray:
         if raw.dtype != np.uint8:
             raise TypeError("E4M3 caches hold uint8 bytes")
         return _E4M3[raw]
+    if kv_format == "e5m2":
+        if raw.dtype != np.uint8:
+            raise TypeError("E5M2 caches hold uint8 bytes")
+        return _E5M2[raw]
     if kv_format == "fp16":
         if raw.dtype != np.float16:
             raise TypeError("FP16 caches hold float16 elements")

@@ -3,8 +3,8 @@
 Written separately from ``oracle/`` from the plain definition
 softmax(sm_scale * Q . (k_scale*K)^T) (v_scale*V) over the keys each verify token sees,
 with the query head h reading KV head h // (Hq/Hkv) and logical token j read from
-physical page block_table[b][j // page_size], slot j % page_size. E4M3 bytes are
-decoded by torch's float8_e4m3fn (a library routine), not by the oracle's table.
+physical page block_table[b][j // page_size], slot j % page_size. E4M3 and E5M2 bytes are
+decoded by torch's float8_e4m3fn / float8_e5m2 (library routines), not by the oracle's tables.
 Only for tiny inputs.
 """
 import math
@@ -15,6 +15,9 @@ import torch
 def _decoder(kv_format):
     if kv_format == "e4m3":
         vals = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).tolist()
+        return lambda x: vals[int(x)]
+    if kv_format == "e5m2":
+        vals = torch.arange(256, dtype=torch.uint8).view(torch.float8_e5m2).to(torch.float64).tolist()
         return lambda x: vals[int(x)]
     return lambda x: float(x)
 

@@ -43,6 +43,8 @@ BRUTE_CASES = [
          kv_format="fp16", seed=14),
     dict(batch=3, seq_lens=[40, 16, 1], q_len=8, num_q_heads=6, num_kv_heads=2, head_dim=8, page_size=32,
          seed=15, kv_scale=0.75),
+    dict(batch=2, seq_lens=[29, 8], q_len=8, num_q_heads=6, num_kv_heads=1, head_dim=16, page_size=16,
+         kv_format="e5m2", seed=16, kv_scale=1.5),
 ]
 
 
@@ -207,6 +209,11 @@ def test_mutation_wrong_exponent_bias_is_caught(monkeypatch):
     bad = np.array([oracle.decode_byte(b) * 0.5 for b in range(256)])     # bias 8 instead of 7
     monkeypatch.setattr(oa, "_E4M3", bad)
     assert _brute_mismatch(BRUTE_CASES[1])
+
+
+def test_mutation_e5m2_read_as_e4m3_is_caught(monkeypatch):
+    monkeypatch.setattr(oa, "_E5M2", oa._E4M3)
+    assert _brute_mismatch(BRUTE_CASES[5])
 
 
 def test_mutation_page_slot_swap_is_caught(monkeypatch):

@@ -34,7 +34,7 @@ class Workload:
     num_kv_heads: int
     head_dim: int
     page_size: int
-    kv_format: str                  # "e4m3" or "fp16"
+    kv_format: str                  # "e4m3", "e5m2" or "fp16"
     kv_std: float                   # K/V values before quantisation are N(0, kv_std**2)
     kv_scale: float                 # per-tensor k_scale = v_scale
     layers: int                     # independent per-layer caches
@@ -68,6 +68,14 @@ def quantize_e4m3(x: torch.Tensor) -> torch.Tensor:
     return x.to(torch.float8_e4m3fn).view(torch.uint8)
 
 
+def quantize_e5m2(x: torch.Tensor) -> torch.Tensor:
+    """float tensor -> uint8 E5M2 (OCP) bytes, round-to-nearest-even via torch."""
+    return x.to(torch.float8_e5m2).view(torch.uint8)
+
+
+ELEMENT_BYTES = {"e4m3": 1, "e5m2": 1, "fp16": 2}
+
+
 def _gen(seed: int, device) -> torch.Generator:
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
@@ -91,15 +99,18 @@ def mixed_lengths(batch: int, seed: int, *, max_len: int = MAX_SEQ_LEN, zero_row
 
 def random_cache(num_pages: int, page_size: int, num_kv_heads: int, head_dim: int, *, kv_format: str,
                  std: float, seed: int, device="cpu", chunk_pages: int = 64) -> torch.Tensor:
-    """[num_pages][page_size][Hkv][D] cache of N(0, std^2) draws, as E4M3 bytes or FP16."""
-    dtype = torch.uint8 if kv_format == "e4m3" else torch.float16
+    """[num_pages][page_size][Hkv][D] cache of N(0, std^2) draws, as E4M3 / E5M2 bytes or FP16."""
+    if kv_format not in ELEMENT_BYTES:
+        raise ValueError(f"unknown kv_format {kv_format!r}")
+    dtype = torch.uint8 if ELEMENT_BYTES[kv_format] == 1 else torch.float16
+    quant = {"e4m3": quantize_e4m3, "e5m2": quantize_e5m2, "fp16": lambda t: t.to(torch.float16)}[kv_format]
     out = torch.empty((num_pages, page_size, num_kv_heads, head_dim), dtype=dtype, device=device)
     g = _gen(seed, device)
     for p0 in range(0, num_pages, chunk_pages):
         p1 = min(num_pages, p0 + chunk_pages)
         x = torch.randn((p1 - p0, page_size, num_kv_heads, head_dim), generator=g, device=device,
                         dtype=torch.float32) * std
-        out[p0:p1] = quantize_e4m3(x) if kv_format == "e4m3" else x.to(torch.float16)
+        out[p0:p1] = quant(x)
     return out
 
 
