@@ -98,7 +98,7 @@ def cpu_baseline(w, case, budget_s: float = 15.0):
                                 float(c["k_scale"][0]), float(c["v_scale"][0]), page_size=c["page_size"],
                                 kv_format=c["kv_format"], pairs=[pair])
         t_total += time.perf_counter() - t0
-        bytes_total += wl.kv_bytes([lens[pair[0]]], 1, w.head_dim, 1 if w.kv_format == "e4m3" else 2)
+        bytes_total += wl.kv_bytes([lens[pair[0]]], 1, w.head_dim, wl.ELEMENT_BYTES[w.kv_format])
         done.append(pair)
         if t_total >= budget_s:
             break
@@ -144,12 +144,17 @@ def main():
     outs = [torch.empty_like(c["q"]) for c in layers]
     arglist = [plan.make_args(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"], c["k_scale"],
                               c["v_scale"], o, ws) for c, o in zip(layers, outs)]
-    elem = 1 if w.kv_format == "e4m3" else 2
+    elem = wl.ELEMENT_BYTES[w.kv_format]
     lens = [int(x) for x in c0["seq_lens"].cpu().tolist()]
     kv_bytes = wl.kv_bytes(lens, w.num_kv_heads, w.head_dim, elem)
     token_heads = sum(lens) * w.num_kv_heads
-    # split_kernel<format, row tiles>: format 0 = E4M3 D256, 1 = FP16 D128; 16 packed rows per tile
-    kernel_name = f"split_kernel<{0 if w.kv_format == 'e4m3' else 1}, {-(-plan.info['rows'] // 16)}>"
+    # split_kernel<format, row tiles, KV heads per workgroup>: format 0 = E4M3 D256, 1 = FP16 D128,
+    # 2 = E5M2 D256; 16 packed rows per tile; heads are paired when Hkv is even and the paired
+    # grid still covers every CU (the library's rule).
+    fmt = {"e4m3": 0, "fp16": 1, "e5m2": 2}[w.kv_format]
+    gs = plan.info["grid_splits"]
+    hp = 2 if w.num_kv_heads % 2 == 0 and w.batch * (w.num_kv_heads // 2) * gs >= plan.info["num_cus"] else 1
+    kernel_name = f"split_kernel<{fmt}, {-(-plan.info['rows'] // 16)}, {hp}>"
 
     def step(i):
         a = arglist[i % w.layers]

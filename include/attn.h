@@ -11,7 +11,9 @@
  * last q_len positions of the sequence), every j < L otherwise. A row that sees no key (L == 0,
  * padded slots, or t < q_len - L) is written as +0. K_j / V_j are the elements of KV head g
  * of logical token j, stored in physical page block_table[b][j / page_size] at slot
- * j % page_size, decoded from E4M3 bytes (OCP E4M3 without infinities, bias 7) or FP16.
+ * j % page_size, decoded from E4M3 bytes (OCP E4M3 without infinities, bias 7), E5M2 bytes
+ * (OCP E5M2, bias 15) or FP16. The pages name E5M2 and FP16 KV as the other cache formats the
+ * backend serves ("DFlash2 ...", same section below).
  *
  * Sources (pages of the method):
  *  - "DFlash2 concurrent long-context attention, 2026-09-27" (design note), section "Why the
@@ -31,8 +33,8 @@
  *    the query heads of one KV group are packed into one block so KV is read once per group;
  *    split partials are merged by a log-sum-exp combine.
  *
- * Execution model. attn_run launches one split-KV kernel: a workgroup per (slot, KV head,
- * split) reads that split's token range once for all q_len*G packed rows and writes an FP32
+ * Execution model. attn_run launches one split-KV kernel: two waves per (slot, KV head,
+ * split) read that split's token range once for all q_len*G packed rows and write an FP32
  * partial (running max, running sum, unnormalised output) into the caller's workspace.
  * attn_combine then merges the splits of each (slot, KV head) in split order and writes FP16.
  * The split count of a row depends only on its own length and on the plan (never on the batch
@@ -71,7 +73,8 @@ typedef enum attn_status {
 
 typedef enum attn_kv_dtype {
     ATTN_KV_E4M3 = 1,        /* one byte per element, OCP E4M3 (no infinities, NaN = S.1111.111) */
-    ATTN_KV_FP16 = 2         /* IEEE binary16 */
+    ATTN_KV_FP16 = 2,        /* IEEE binary16 */
+    ATTN_KV_E5M2 = 3         /* one byte per element, OCP E5M2 (the upper byte of an FP16 value) */
 } attn_kv_dtype;
 
 /* One supported (kv_dtype, head_dim) combination and its row limits. */

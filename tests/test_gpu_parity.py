@@ -37,6 +37,40 @@ def test_e4m3_bytes_decode_exactly():
         assert torch.equal(out[0, 0, h][nonzero].view(torch.int16), want[nonzero].view(torch.int16)), h
 
 
+def test_e5m2_bytes_decode_exactly():
+    # As above for E5M2: the only visible key's V row holds all 248 finite E5M2 bytes (up to
+    # +-57344 and down to the subnormal 2^-16), so the output is exactly those FP16 values.
+    note("e5m2 all bytes, B1 L8 Hq6 Hkv1 page16")
+    c = _case(batch=1, seq_lens=[8], q_len=8, num_q_heads=6, num_kv_heads=1, head_dim=256, page_size=16, seed=102,
+              kv_format="e5m2")
+    vals = np.arange(256, dtype=np.uint8)
+    vals[[0x7C, 0x7D, 0x7E, 0x7F, 0xFC, 0xFD, 0xFE, 0xFF]] = 0
+    page = int(c["block_table"][0, 0])
+    c["v_cache"][page, 0, 0, :] = torch.from_numpy(vals).cuda()
+    out = run_gpu(c)
+    want = torch.from_numpy(oracle.decode_e5m2_table()[vals].astype(np.float16)).cuda()
+    for h in range(6):
+        assert torch.equal(out[0, 0, h], want), h
+        nonzero = want != 0
+        assert torch.equal(out[0, 0, h][nonzero].view(torch.int16), want[nonzero].view(torch.int16)), h
+
+
+E5M2_SMALL = [
+    dict(batch=2, seq_lens=[5, 700], q_len=8, num_q_heads=6, num_kv_heads=1, page_size=16),
+    dict(batch=3, seq_lens=[2000, 33, 0], q_len=8, num_q_heads=24, num_kv_heads=4, page_size=1648, kv_std=0.5,
+         kv_scale=2.0),
+    dict(batch=2, seq_lens=[9000, 300], q_len=4, num_q_heads=16, num_kv_heads=4, page_size=32),
+]
+
+
+@pytest.mark.parametrize("kw", E5M2_SMALL, ids=lambda kw: f"e5m2-B{kw['batch']}-L{max(kw['seq_lens'])}-q{kw['q_len']}-"
+                                                           f"H{kw['num_q_heads']}/{kw['num_kv_heads']}")
+def test_parity_e5m2(kw):
+    note(f"parity e5m2 {kw}")
+    c = _case(head_dim=256, kv_format="e5m2", seed=sum(kw["seq_lens"]) + 5, **kw)
+    compare(run_gpu(c), run_oracle(c))
+
+
 SMALL = [
     dict(batch=1, seq_lens=[1], q_len=8, num_q_heads=6, num_kv_heads=1, page_size=16),
     dict(batch=1, seq_lens=[8], q_len=8, num_q_heads=6, num_kv_heads=1, page_size=16),
@@ -128,7 +162,7 @@ def test_fp16_values_pass_through_exactly():
 
 
 @pytest.mark.parametrize("name", ["verify_b1_ctx3297_hq6_hkv1", "verify_b4_ctx32k_gqa6",
-                                  "decode_b8_ctx32k_d128_fp16_gqa4"])
+                                  "decode_b8_ctx32k_d128_fp16_gqa4", "verify_b4_ctx32k_gqa6_e5m2"])
 def test_parity_workload_full(name):
     note(f"parity full workload {name}")
     w = wl.WORKLOADS[name]

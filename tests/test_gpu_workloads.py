@@ -1,5 +1,5 @@
 """GPU parity at the full sizes of the long-context workloads, in the launch configuration the
-benchmark times: B8 x 131072 (sampled (slot, KV head) pairs checked against the oracle) and
+benchmark times: B8 x 131072, E4M3 and E5M2 (sampled (slot, KV head) pairs checked against the oracle) and
 B16 mixed lengths up to 262144 with page 3296, captured once in a graph and replayed with
 fresh queries, lengths and zero rows."""
 import numpy as np
@@ -12,8 +12,9 @@ from verify_attention_e4m3_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 
 
-def test_b8_ctx128k_sampled_pairs():
-    w = wl.WORKLOADS["verify_b8_ctx128k_gqa6_16layers"]
+@pytest.mark.parametrize("name", ["verify_b8_ctx128k_gqa6_16layers", "verify_b8_ctx128k_gqa6_e5m2_16layers"])
+def test_b8_ctx128k_sampled_pairs(name):
+    w = wl.WORKLOADS[name]
     note(f"{w.name} layer 0, sampled pairs")
     c = wl.workload_case(w, device="cuda", layer=0)
     plan = plan_for(c)

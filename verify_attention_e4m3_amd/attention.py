@@ -23,12 +23,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so"
 
 ATTN_ABI_VERSION = 1
 ATTN_OK, ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_HIP, ATTN_E_WORKSPACE = range(5)
-ATTN_KV_E4M3, ATTN_KV_FP16 = 1, 2
+ATTN_KV_E4M3, ATTN_KV_FP16, ATTN_KV_E5M2 = 1, 2, 3
 ATTN_DEVICE_HOST_ONLY = -1
 ATTN_MAX_GEOMETRIES = 8
 
-KV_DTYPES = {"e4m3": ATTN_KV_E4M3, "fp16": ATTN_KV_FP16}
-ELEM_BYTES = {"e4m3": 1, "fp16": 2}
+KV_DTYPES = {"e4m3": ATTN_KV_E4M3, "fp16": ATTN_KV_FP16, "e5m2": ATTN_KV_E5M2}
+ELEM_BYTES = {"e4m3": 1, "fp16": 2, "e5m2": 1}
 
 
 class attn_geometry(ctypes.Structure):

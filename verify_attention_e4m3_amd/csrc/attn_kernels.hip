@@ -75,41 +75,65 @@ constexpr int kMaxSplitPages = 32768 / 16 + 2;
 struct TileK { u32x4 k[2][4]; };
 struct TileV { u32x4 v[8]; };
 
-// KV element formats whose token rows of one head are 256 bytes: E4M3 at D = 256 and FP16 at
-// D = 128. They share the gather, the LDS ring and the swizzle; they differ in how a lane's 16
-// bytes become MFMA operands and which output dims an accumulator element holds.
-enum KvFormat { kFmtE4M3D256 = 0, kFmtF16D128 = 1 };
+// KV element formats whose token rows of one head are 256 bytes: E4M3 and E5M2 at D = 256 and
+// FP16 at D = 128. They share the gather, the LDS ring and the swizzle; they differ in how a
+// lane's 16 bytes become MFMA operands and which output dims an accumulator element holds.
+enum KvFormat { kFmtE4M3D256 = 0, kFmtF16D128 = 1, kFmtE5M2D256 = 2 };
 
-template <int FMT> struct Fmt;
+// Byte -> FP16 decoders of the one-byte formats; both are exact.
+// E4M3: v_cvt_scalef32_pk_f16_fp8 with scale 1.0 (every finite E4M3 value is an FP16 value).
+struct DecE4M3 {
+    __device__ static half8 x8(uint32_t lo, uint32_t hi) { return e4m3x8(lo, hi); }
+    // Byte pair cp of the dwords a (token 2pp) and b (token 2pp+1): FP16 pairs (a, b) of dims
+    // 2cp (d0) and 2cp+1 (d1).
+    __device__ static void pair(uint32_t b, uint32_t a, int cp, half2v& d0, half2v& d1) {
+        const uint32_t pr = __builtin_amdgcn_perm(b, a, cp ? 0x07030602u : 0x05010400u);
+        d0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pr, 1.0f, false);
+        d1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pr, 1.0f, true);
+    }
+};
 
-// E4M3, D = 256. K vector i of a lane holds dims 64*i + 16*qd + 0..15 (one byte each) and
-// feeds k-steps 2i and 2i+1; PV MFMA j (0..15) covers dims 16*m + j.
-template <> struct Fmt<kFmtE4M3D256> {
+// E5M2 has FP16's sign, exponent width and bias, so a byte is the upper byte of the FP16 value
+// it encodes (subnormals, infinities and NaN included): decoding is a byte permute that puts
+// each byte over a zero byte (selector 0x0c yields 0x00).
+struct DecE5M2 {
+    __device__ static half8 x8(uint32_t lo, uint32_t hi) {
+        const u32x4 w = {__builtin_amdgcn_perm(0u, lo, 0x010c000cu), __builtin_amdgcn_perm(0u, lo, 0x030c020cu),
+                         __builtin_amdgcn_perm(0u, hi, 0x010c000cu), __builtin_amdgcn_perm(0u, hi, 0x030c020cu)};
+        return __builtin_bit_cast(half8, w);
+    }
+    __device__ static void pair(uint32_t b, uint32_t a, int cp, half2v& d0, half2v& d1) {
+        d0 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(b, a, cp ? 0x060c020cu : 0x040c000cu));
+        d1 = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(b, a, cp ? 0x070c030cu : 0x050c010cu));
+    }
+};
+
+// One-byte formats, D = 256. K vector i of a lane holds dims 64*i + 16*qd + 0..15 (one byte
+// each) and feeds k-steps 2i and 2i+1; PV MFMA j (0..15) covers dims 16*m + j.
+template <class Dec>
+struct Fmt8D256 {
     static constexpr int D = 256;
     static constexpr int KSTEPS = 8;
     static constexpr int JT = 16;
     __device__ static int q_dim(int ks, int qd) { return 64 * (ks >> 1) + 16 * qd + 8 * (ks & 1); }
     __device__ static half8 k_op(const u32x4 (&k)[4], int ks) {
         const u32x4 w = k[ks >> 1];
-        return (ks & 1) ? e4m3x8(w[2], w[3]) : e4m3x8(w[0], w[1]);
+        return (ks & 1) ? Dec::x8(w[2], w[3]) : Dec::x8(w[0], w[1]);
     }
     __device__ static int o_dim(int qd, int i, int j) { return 16 * (4 * qd + i) + j; }
-    // O^T += V^T . P^T. For dword w of the lane's 16 V bytes and byte pair (2cp, 2cp+1), a byte
-    // permute regroups tokens (2pp, 2pp+1) of dims 16*n + 4*w + 2*cp + {0,1} into 16-bit words,
-    // which convert to the FP16 pairs of the A operand.
+    // O^T += V^T . P^T. For dword w of the lane's 16 V bytes and byte pair (2cp, 2cp+1), tokens
+    // (2pp, 2pp+1) of dims 16*n + 4*w + 2*cp + {0,1} become the FP16 pairs of the A operand.
     template <int RT>
     __device__ static void pv(const TileV& t, const half8 (&pop)[RT], float4v (&o)[RT][JT]) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
 #pragma unroll
             for (int cp = 0; cp < 2; ++cp) {
-                const uint32_t sel = cp ? 0x07030602u : 0x05010400u;
                 half8 a0, a1;
 #pragma unroll
                 for (int pp = 0; pp < 4; ++pp) {
-                    const uint32_t pr = __builtin_amdgcn_perm(t.v[2 * pp + 1][w], t.v[2 * pp][w], sel);
-                    const half2v lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pr, 1.0f, false);
-                    const half2v hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pr, 1.0f, true);
+                    half2v lo, hi;
+                    Dec::pair(t.v[2 * pp + 1][w], t.v[2 * pp][w], cp, lo, hi);
                     a0[2 * pp] = lo[0];
                     a0[2 * pp + 1] = lo[1];
                     a1[2 * pp] = hi[0];
@@ -125,6 +149,10 @@ template <> struct Fmt<kFmtE4M3D256> {
         }
     }
 };
+
+template <int FMT> struct Fmt;
+template <> struct Fmt<kFmtE4M3D256> : Fmt8D256<DecE4M3> {};
+template <> struct Fmt<kFmtE5M2D256> : Fmt8D256<DecE5M2> {};
 
 // FP16, D = 128. K vector i of a lane holds dims 32*i + 8*qd + 0..7 and is k-step i as it is;
 // PV MFMA j (0..7) covers dims 8*m + j.
@@ -776,8 +804,9 @@ attn_status attn_launch_split(const attn_plan_s* plan, const attn::RunParams& p,
     void* kargs[] = {&args};
     const int row_tiles = p.rows_alloc / 16;
     const int hp = attn::heads_per_workgroup(p.num_kv_heads, p.batch, p.grid_splits, plan->num_cus);
-    attn::KernelFn fn = plan->desc.kv_dtype == ATTN_KV_FP16 ? attn::split_for<attn::kFmtF16D128>(row_tiles, hp)
-                                                             : attn::split_for<attn::kFmtE4M3D256>(row_tiles, hp);
+    attn::KernelFn fn = plan->desc.kv_dtype == ATTN_KV_FP16   ? attn::split_for<attn::kFmtF16D128>(row_tiles, hp)
+                        : plan->desc.kv_dtype == ATTN_KV_E5M2 ? attn::split_for<attn::kFmtE5M2D256>(row_tiles, hp)
+                                                              : attn::split_for<attn::kFmtE4M3D256>(row_tiles, hp);
     // One workgroup per (slot, split, group of hp KV heads); the kernel decodes the same order.
     const unsigned grid = (unsigned)p.batch * (p.num_kv_heads / hp) * p.grid_splits;
     hipError_t e = hipLaunchKernel((const void*)fn, dim3(grid), dim3(64 * attn::kWavesPerHead * hp), kargs, 0,

@@ -27,6 +27,7 @@ struct Geometry {
 constexpr Geometry kGeometries[] = {
     {ATTN_KV_E4M3, 256, 8, attn::kMaxRows},
     {ATTN_KV_FP16, 128, 8, attn::kMaxRows},
+    {ATTN_KV_E5M2, 256, 8, attn::kMaxRows},
 };
 constexpr int kNumGeometries = sizeof(kGeometries) / sizeof(kGeometries[0]);
 
@@ -74,7 +75,8 @@ attn_status attn_plan(const attn_desc* d, int device, attn_plan_t* out, size_t* 
     if (out) *out = nullptr;
     if (!d || !out) return ATTN_E_INVALID;
     if (d->abi_version != ATTN_ABI_VERSION) return ATTN_E_INVALID;
-    if (d->kv_dtype != ATTN_KV_E4M3 && d->kv_dtype != ATTN_KV_FP16) return ATTN_E_INVALID;
+    if (d->kv_dtype != ATTN_KV_E4M3 && d->kv_dtype != ATTN_KV_FP16 && d->kv_dtype != ATTN_KV_E5M2)
+        return ATTN_E_INVALID;
     if (d->q_len < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->head_dim < 1) return ATTN_E_INVALID;
     if (d->num_q_heads % d->num_kv_heads != 0) return ATTN_E_INVALID;
     if (d->page_size < 1 || d->page_size % attn::kPageAlign != 0) return ATTN_E_INVALID;
