@@ -95,6 +95,24 @@ def test_parity_small(kw):
     assert stats["rows"] > 0
 
 
+@pytest.mark.parametrize("q_len", range(1, 9))
+def test_parity_every_q_len(q_len):
+    # q-generic verify: batched q1..q8 with six query heads per KV head (6..48 packed rows, so
+    # one, two and three row tiles), lengths around and below q.
+    note(f"parity q_len {q_len}, B4 Hq12/Hkv2")
+    c = _case(batch=4, seq_lens=[1500, q_len, max(q_len - 1, 0), 4097], q_len=q_len, num_q_heads=12,
+              num_kv_heads=2, head_dim=256, page_size=32, seed=200 + q_len)
+    compare(run_gpu(c), run_oracle(c))
+
+
+@pytest.mark.parametrize("q_len", [1, 3, 8])
+def test_parity_four_query_heads_on_one_kv_head(q_len):
+    note(f"parity Hq4/Hkv1 q_len {q_len}")
+    c = _case(batch=3, seq_lens=[3297, 100, 7], q_len=q_len, num_q_heads=4, num_kv_heads=1, head_dim=256,
+              page_size=1648, seed=210 + q_len)
+    compare(run_gpu(c), run_oracle(c))
+
+
 def test_parity_non_causal_and_custom_scale():
     note("parity non-causal, sm_scale 0.05")
     c = _case(batch=2, seq_lens=[77, 1500], q_len=8, num_q_heads=6, num_kv_heads=1, head_dim=256, page_size=16,
