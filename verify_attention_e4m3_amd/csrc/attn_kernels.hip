@@ -11,24 +11,27 @@
 // "Scope" (FP16 operands, FP32 accumulation for QK and PV) and "Implementation and validation
 // in progress" (exact E4M3 -> FP16 conversion).
 //
-// Kernel design (one 64-lane wave per workgroup and per (slot, KV head, split)):
-//  * The 48 packed rows (8 verify tokens x 6 heads) are the N dimension of every MFMA, so one
-//    wave reads each K/V byte of its token range exactly once for all rows.
+// Kernel design (two 64-lane waves per (slot, KV head, split); one or two KV heads per
+// workgroup):
+//  * The packed rows (q_len verify tokens x G heads, up to 48) are the N dimension of every
+//    MFMA, so each K/V byte of a token range is read exactly once for all rows.
 //  * S^T = K . Q^T on v_mfma_f32_16x16x32_f16: A = 16 tokens x 32 dims of K, B = 32 dims x 16
 //    rows of Q (Q stays in registers for the whole split). The dims are visited in a
 //    permuted order shared by A and B, chosen so each lane's K bytes are 4 contiguous 16-byte
 //    loads; a contraction is indifferent to the order.
 //  * O^T += V^T . P^T on the same MFMA: A = 16 dims x 32 tokens of V, B = 32 tokens x 16 rows
 //    of P. The token order is the one the S^T accumulators already hold, so P feeds the
-//    second MFMA straight from registers; MFMA j of a lane covers dims 16*m + j, so each lane
-//    loads 16 contiguous V bytes per token and a byte permute regroups them per dim.
-//  * Row ownership is identical in both products (row = lane % 16), so the running max/sum
-//    and the O rescale stay lane-local; the max is reduced across the 4 lanes of a row.
-//  * E4M3 -> FP16 is exact (every finite E4M3 value is an FP16 value); k_scale is folded into
-//    the FP32 score scale and v_scale is applied once in the combine.
-//  * Each split writes an FP32 panel {O[48][D], m[48], l[48]} (m in log2 units of the scaled
-//    score). The combine merges a row's splits in split order - no atomics, so results are
-//    bitwise reproducible and independent of the batch a request is in.
+//    second MFMA straight from registers; each lane loads 16 contiguous V bytes per token and
+//    a byte permute regroups them per dim.
+//  * Row ownership is identical in both products (row = lane % 16), so the softmax statistics
+//    stay lane-local; the max is reduced across the 4 lanes of a row. Exponentials use a fixed
+//    per-row reference (with a recompute pass if a later tile exceeds it by too much), so the
+//    O accumulators are never rescaled.
+//  * E4M3 / E5M2 -> FP16 are exact (every finite value of either is an FP16 value); k_scale is
+//    folded into the FP32 score scale and v_scale is applied once in the combine.
+//  * Each split writes an FP32 panel {O[rows][D], m[rows], l[rows]} (m in log2 units of the
+//    scaled score). The combine merges a row's splits in split order - no atomics, so results
+//    are bitwise reproducible and independent of the batch a request is in.
 #include <hip/hip_runtime.h>
 
 #include "attn_internal.h"
