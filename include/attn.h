@@ -194,6 +194,40 @@ ATTN_API attn_status attn_combine(attn_plan_t plan, const attn_args* args, void*
 /* Static text for a status code (never NULL). */
 ATTN_API const char* attn_status_string(attn_status status);
 
+/*
+ * Long prefill. Causal attention of a chunk of q_len query tokens against a kv_len-token
+ * sequence whose last q_len positions they are: query token t of head h sees keys
+ * j <= kv_len - q_len + t (every key when causal == 0), K/V head g = h / (Hq / Hkv). FP16 Q, K,
+ * V and output, D = 256, FP32 accumulation for QK and PV. Source: "SM70 attention and
+ * quantized projection coverage across TP sizes", sections "Scope" and "Accumulation audit and
+ * rejected tuning" (the Q8192 x KV262144 prefill of six query heads per KV head, a full prefix
+ * plus a causal triangular tail, FP32 accumulation in both products).
+ *
+ * Layout: element (token, head, d) of Q / K / V / out is at base + token * token_stride +
+ * head * head_stride + d (strides in elements, multiples of 8; bases 16-byte aligned; K/V tokens
+ * contiguous in one buffer per tensor). Errors: ATTN_E_INVALID for null pointers, bad strides,
+ * sizes or ABI version; ATTN_E_UNSUPPORTED unless head_dim == 256 and Hq / Hkv divides 12;
+ * ATTN_E_HIP if the launch fails. Stateless: no plan, no workspace; the library allocates
+ * nothing and does not synchronise. Rows that see no key are +0.
+ */
+typedef struct attn_prefill_desc {
+    uint32_t abi_version;        /* ATTN_ABI_VERSION */
+    int32_t q_len;               /* query tokens (>= 1) */
+    int32_t kv_len;              /* keys (>= 1); queries are its last q_len positions */
+    int32_t num_q_heads;         /* Hq */
+    int32_t num_kv_heads;        /* Hkv, Hq % Hkv == 0 */
+    int32_t head_dim;            /* 256 */
+    int64_t q_token_stride, q_head_stride;   /* elements */
+    int64_t k_token_stride, k_head_stride;
+    int64_t v_token_stride, v_head_stride;
+    int64_t o_token_stride, o_head_stride;
+    float sm_scale;              /* 0 selects 1 / sqrt(head_dim) */
+    int32_t causal;              /* 1 or 0 */
+} attn_prefill_desc;
+
+ATTN_API attn_status attn_prefill(const attn_prefill_desc* desc, const void* q, const void* k, const void* v,
+                                  void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

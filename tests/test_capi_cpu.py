@@ -20,7 +20,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     lib = A.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -38,11 +38,13 @@ def test_struct_layout_matches_the_header(tmp_path):
 #include "attn.h"
 #define F(T, m) printf(#T "." #m " %zu\n", offsetof(T, m))
 int main(void) {
-  printf("attn_desc %zu\nattn_args %zu\nattn_caps %zu\nattn_plan_info %zu\n",
-         sizeof(attn_desc), sizeof(attn_args), sizeof(attn_caps), sizeof(attn_plan_info));
+  printf("attn_desc %zu\nattn_args %zu\nattn_caps %zu\nattn_plan_info %zu\nattn_prefill_desc %zu\n",
+         sizeof(attn_desc), sizeof(attn_args), sizeof(attn_caps), sizeof(attn_plan_info), sizeof(attn_prefill_desc));
   F(attn_desc, k_page_stride); F(attn_desc, v_head_stride); F(attn_desc, sm_scale); F(attn_desc, causal);
   F(attn_args, num_pages); F(attn_args, workspace_bytes); F(attn_args, out); F(attn_args, batch);
   F(attn_caps, geometries); F(attn_plan_info, split_bytes);
+  F(attn_prefill_desc, q_token_stride); F(attn_prefill_desc, o_head_stride); F(attn_prefill_desc, sm_scale);
+  F(attn_prefill_desc, causal);
   return 0;
 }
 ''')
@@ -54,6 +56,7 @@ int main(void) {
     assert int(got["attn_args"]) == ctypes.sizeof(A.attn_args)
     assert int(got["attn_caps"]) == ctypes.sizeof(A.attn_caps)
     assert int(got["attn_plan_info"]) == ctypes.sizeof(A.attn_plan_info)
+    assert int(got["attn_prefill_desc"]) == ctypes.sizeof(A.attn_prefill_desc)
     for key, val in got.items():
         if "." in key:
             struct, field = key.split(".")
@@ -221,3 +224,40 @@ def test_workspace_is_request_major():
     assert p.info["split_bytes"] >= (48 * 256 + 96) * 4
     for b in range(1, 9):
         assert p.workspace_bytes(b) == b * per_slot
+
+
+# ---- long prefill: admission is host-only, so it can be checked without a GPU ----
+
+def _pf_desc(**kw):
+    base = dict(abi_version=A.ATTN_ABI_VERSION, q_len=100, kv_len=300, num_q_heads=12, num_kv_heads=2, head_dim=256,
+                q_token_stride=12 * 256, q_head_stride=256, k_token_stride=2 * 256, k_head_stride=256,
+                v_token_stride=2 * 256, v_head_stride=256, o_token_stride=12 * 256, o_head_stride=256,
+                sm_scale=0.0, causal=1)
+    base.update(kw)
+    return A.attn_prefill_desc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=128), A.ATTN_E_UNSUPPORTED),
+    (dict(num_q_heads=10), A.ATTN_E_UNSUPPORTED),          # G = 5 does not divide the 12 row tiles
+    (dict(num_q_heads=13), A.ATTN_E_INVALID),              # Hq % Hkv != 0
+    (dict(q_len=0), A.ATTN_E_INVALID),
+    (dict(kv_len=0), A.ATTN_E_INVALID),
+    (dict(k_token_stride=2 * 256 + 4), A.ATTN_E_INVALID),  # not a multiple of 8 elements
+    (dict(causal=2), A.ATTN_E_INVALID),
+    (dict(sm_scale=-1.0), A.ATTN_E_INVALID),
+    (dict(sm_scale=float("nan")), A.ATTN_E_INVALID),
+    (dict(abi_version=7), A.ATTN_E_INVALID),
+    (dict(k_token_stride=1 << 26), A.ATTN_E_INVALID),      # 64-key block offsets would overflow 32 bits
+])
+def test_prefill_admission_rejects(kw, status):
+    d = _pf_desc(**kw)
+    assert A.lib().attn_prefill(ctypes.byref(d), 4096, 8192, 12288, 16384, None) == status
+
+
+def test_prefill_rejects_null_and_misaligned_pointers():
+    d = _pf_desc()
+    lib = A.lib()
+    assert lib.attn_prefill(None, 4096, 8192, 12288, 16384, None) == A.ATTN_E_INVALID
+    assert lib.attn_prefill(ctypes.byref(d), 0, 8192, 12288, 16384, None) == A.ATTN_E_INVALID
+    assert lib.attn_prefill(ctypes.byref(d), 4096 + 8, 8192, 12288, 16384, None) == A.ATTN_E_INVALID

@@ -67,6 +67,16 @@ class attn_args(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t), ("out", ctypes.c_void_p), ("batch", ctypes.c_int32)]
 
 
+class attn_prefill_desc(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_uint32), ("q_len", ctypes.c_int32), ("kv_len", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("q_token_stride", ctypes.c_int64), ("q_head_stride", ctypes.c_int64),
+                ("k_token_stride", ctypes.c_int64), ("k_head_stride", ctypes.c_int64),
+                ("v_token_stride", ctypes.c_int64), ("v_head_stride", ctypes.c_int64),
+                ("o_token_stride", ctypes.c_int64), ("o_head_stride", ctypes.c_int64),
+                ("sm_scale", ctypes.c_float), ("causal", ctypes.c_int32)]
+
+
 EXPORTS = {
     "attn_get_capabilities": (ctypes.c_int, [ctypes.POINTER(attn_caps)]),
     "attn_plan": (ctypes.c_int, [ctypes.POINTER(attn_desc), ctypes.c_int, ctypes.POINTER(ctypes.c_void_p),
@@ -79,6 +89,8 @@ EXPORTS = {
     "attn_run": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(attn_args), ctypes.c_void_p]),
     "attn_combine": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(attn_args), ctypes.c_void_p]),
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "attn_prefill": (ctypes.c_int, [ctypes.POINTER(attn_prefill_desc), ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
 }
 
 _lib = None
@@ -292,3 +304,31 @@ def default_bank() -> WorkspaceBank:
     if _default_bank is None:
         _default_bank = WorkspaceBank()
     return _default_bank
+
+
+def prefill_desc(q, k, v, out, *, causal: bool = True, sm_scale: float = 0.0,
+                 abi_version: int = ATTN_ABI_VERSION) -> attn_prefill_desc:
+    """attn_prefill_desc for [tokens][heads][D] views (element strides taken from the tensors)."""
+    return attn_prefill_desc(abi_version, q.shape[0], k.shape[0], q.shape[1], k.shape[1], q.shape[2],
+                             q.stride(0), q.stride(1), k.stride(0), k.stride(1), v.stride(0), v.stride(1),
+                             out.stride(0), out.stride(1), sm_scale, 1 if causal else 0)
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+            causal: bool = True, sm_scale: float = 0.0, stream=None) -> torch.Tensor:
+    """attn_prefill on FP16 q [q_len][Hq][D], k / v [kv_len][Hkv][D] (any element strides with a
+    unit dim stride); the queries are the last q_len positions of the kv_len-token sequence."""
+    if out is None:
+        out = torch.empty_like(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.dtype != torch.float16 or t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError(f"{name} must be a float16 [tokens][heads][D] view with unit dim stride")
+    if k.shape != v.shape or out.shape != q.shape or q.shape[2] != k.shape[2]:
+        raise ValueError("shape mismatch between q, k, v and out")
+    d = prefill_desc(q, k, v, out, causal=causal, sm_scale=sm_scale)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    _check("attn_prefill", lib().attn_prefill(ctypes.byref(d), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                              out.data_ptr(), st))
+    return out

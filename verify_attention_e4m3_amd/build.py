@@ -12,7 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = [os.path.join(CSRC, "attn_kernels.hip"), os.path.join(CSRC, "attn_plan.cpp")]
+SOURCES = [os.path.join(CSRC, "attn_kernels.hip"), os.path.join(CSRC, "prefill_kernels.hip"),
+           os.path.join(CSRC, "attn_plan.cpp")]
 # Measurement-only library used by bench.py (a plain streaming-read kernel); not the attention ABI.
 PROBE_LIB = os.path.join(PKG, "libattn_probe.so")
 PROBE_SOURCES = [os.path.join(CSRC, "stream_probe.hip")]

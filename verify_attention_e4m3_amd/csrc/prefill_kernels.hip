@@ -1,0 +1,378 @@
+// prefill_kernels.hip - causal long-prefill attention for gfx950 (CDNA4), FP16 Q/K/V, D = 256.
+//
+// What is computed (see include/attn.h, attn_prefill): for query token t in [0, q_len) of head
+// h, with G = Hq / Hkv and KV head g = h / G, softmax(sm_scale * q.K^T) V over the keys the
+// token sees - with the queries being the last q_len positions of a kv_len-token sequence,
+// token t sees keys j <= kv_len - q_len + t (every key when not causal). The long prefill of
+// "SM70 attention and quantized projection coverage across TP sizes" (sections "Scope" and
+// "Accumulation audit and rejected tuning": a Q8192 chunk against a 262144-token context,
+// D = 256, six query heads per KV head, FP16 inputs, FP32 accumulation for both QK and PV, a
+// full-width prefix plus a causal triangular tail).
+//
+// Kernel design (an MFMA-bound dense contraction, unlike the HBM-bound verify kernel):
+//  * A workgroup of 4 waves (one per SIMD) owns 12 row tiles of 16 query rows: 16 consecutive
+//    tokens of one query head each, all heads of one KV head group, so every K/V byte brought
+//    into LDS serves 192 query rows. Wave w owns row tiles 3w .. 3w+2.
+//  * Keys stream in blocks of 32 through a three-stage LDS ring (K and V, 16 KB each per
+//    stage): right after the one barrier of block b all four waves issue direct global -> LDS
+//    loads of block b+2, so two blocks are in flight during block b's math. 16-byte chunks of a
+//    token row are XOR-swizzled by token (chunk ^ token % 16), so the MFMA-order LDS reads of 16
+//    lanes hit 16 different bank groups for both K and V.
+//  * S^T = K . Q^T and O^T += V^T . P^T on v_mfma_f32_16x16x32_f16 with the query rows on the
+//    N dimension: a lane holds one query row in both products, so softmax statistics stay
+//    lane-local apart from a reduction over the 4 lanes of a row, and P feeds the second MFMA
+//    from registers (the PV contraction visits keys in the order S^T holds them). Lane m of the
+//    PV A operand holds dims 8m..8m+7 and 128+8m..128+8m+7 of 8 keys, one 16-byte LDS read per
+//    key and half; a permute pairs keys per dim.
+//  * Softmax in log2 units against a fixed per-row reference (the maximum of the first block in
+//    which the row sees a key), so the O accumulators are only ever touched by MFMAs. A later
+//    block may exceed the reference by up to 2^10 (exact range in FP16 and FP32); if any row of
+//    the workgroup exceeds it by more, the workgroup recomputes with each row's exact maximum
+//    from a QK-only pass. Both passes depend only on the data, so results are deterministic.
+//  * Q (3 row tiles x 256 dims) stays in registers for the whole key loop; O^T (3 x 256 x 16
+//    FP32 per wave) lives in accumulation registers.
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "attn_internal.h"
+#include "prefill_internal.h"
+
+namespace attn {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kPfWaves = 4;
+constexpr int kPfRowTilesPerWave = 3;
+constexpr int kPfBlock = 32;                                 // keys per block: two granules of 16
+constexpr int kPfStages = 3;
+constexpr int kPfD = 256;
+constexpr int kPfRowBytes = kPfD * 2;                        // one token row of one head
+constexpr int kPfStageBytes = kPfBlock * kPfRowBytes;        // 16 KB: one K (or V) block
+constexpr int kPfLoadsPerWave = kPfStageBytes / 1024 / kPfWaves;   // 4 K + 4 V per wave and block
+constexpr float kPfSlack = 10.0f;                            // log2 headroom over the reference
+
+__device__ __forceinline__ uint32_t pf_lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Direct global -> LDS load of 16 bytes per lane from base + voff into lds + 16*lane. Inline asm
+// so that the compiler does not wait for it before every LDS read; the key loop waits
+// explicitly. No streaming hint: every K/V block is read by all workgroups of its KV head.
+__device__ __forceinline__ void pf_dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
+    const uint64_t b64 = (uint64_t)base;
+    const uint64_t sbase = join_words((uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32)),
+                                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64));
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
+                 "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+
+struct PrefillLds {
+    __attribute__((aligned(16))) uint8_t k[kPfStages][kPfStageBytes];
+    __attribute__((aligned(16))) uint8_t v[kPfStages][kPfStageBytes];
+};
+
+// Loads of one key block: 16 instructions for K and 16 for V, each covering two 512-byte token
+// rows; wave w issues instructions 4w .. 4w+3 of both. Lane l of instruction i writes LDS row
+// 2i + l/32, slot l%32, and fetches that row's chunk (l%32) ^ (row%16). Rows past the sequence
+// re-read its last token (they are masked).
+__device__ __forceinline__ void pf_issue_block(const PrefillParams& p, const uint8_t* kbase, const uint8_t* vbase,
+                                               int32_t blk, uint32_t k_stage, uint32_t v_stage, int wave,
+                                               int lane) {
+    const int32_t key0 = blk * kPfBlock;
+    const int32_t last = p.kv_len - 1 - key0;                // last valid row of this block
+    const uint8_t* kb = kbase + (int64_t)key0 * p.k_token_stride * 2;
+    const uint8_t* vb = vbase + (int64_t)key0 * p.v_token_stride * 2;
+    const int slot = lane & 31;
+#pragma unroll
+    for (int u = 0; u < kPfLoadsPerWave; ++u) {
+        const int i = wave * kPfLoadsPerWave + u;
+        const int row = 2 * i + (lane >> 5);
+        const int src_row = min(row, last);
+        const uint32_t chunk = (uint32_t)(slot ^ (row & 15)) * 16;
+        pf_dma16(kb, (uint32_t)(src_row * p.k_token_stride * 2) + chunk, k_stage + i * 1024);
+        pf_dma16(vb, (uint32_t)(src_row * p.v_token_stride * 2) + chunk, v_stage + i * 1024);
+    }
+}
+
+__device__ __forceinline__ void pf_wait_block(bool next_in_flight) {
+    if (next_in_flight) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // block b+1's 8 loads may remain
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+__global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p) {
+    constexpr int RT = kPfRowTilesPerWave;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15;         // MFMA column: query row within a row tile
+    const int qd = lane >> 4;        // quarter of the wave
+
+    // Workgroup order: KV head fastest, then query tile.
+    const int g = blockIdx.x % p.num_kv_heads;
+    const int qt = blockIdx.x / p.num_kv_heads;
+    const int32_t t0 = qt * p.tokens_per_wg;
+
+    // Row tile r (0..11) of the workgroup: query tokens t0 + 16*(r / G) + 0..15 of head g*G + r%G.
+    half8 qop[RT][8];
+    int32_t lim[RT];                 // keys j < lim[rt] are visible to this lane's row
+    int32_t tok[RT], head[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int r = wave * RT + rt;
+        const int tg = r / p.group;
+        head[rt] = g * p.group + (r - tg * p.group);
+        tok[rt] = t0 + 16 * tg + n;
+        const bool live = tok[rt] < p.q_len;
+        const uint16_t* qrow =
+            p.q + (int64_t)(live ? tok[rt] : 0) * p.q_token_stride + (int64_t)head[rt] * p.q_head_stride;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const half8 v = *reinterpret_cast<const half8*>(qrow + 32 * ks + 8 * qd);
+            qop[rt][ks] = live ? v : half8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+        const int32_t vis = p.causal ? p.kv_len - p.q_len + tok[rt] + 1 : p.kv_len;
+        lim[rt] = live ? max(0, min(vis, p.kv_len)) : 0;
+    }
+    // Make the Q loads land before the ring is primed (their waits would otherwise count the
+    // ring's loads).
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ks = 0; ks < 8; ks += 2) asm volatile("" ::"v"(qop[rt][ks]), "v"(qop[rt][ks + 1]));
+
+    // Keys the workgroup needs: up to the last visible key of its last live token. Blocks that
+    // end below every row's limit need no mask.
+    const int32_t t_last = min(t0 + p.tokens_per_wg, p.q_len) - 1;
+    const int32_t key_end = p.causal ? min(p.kv_len, p.kv_len - p.q_len + t_last + 1) : p.kv_len;
+    const int32_t nblk = key_end > 0 ? (key_end + kPfBlock - 1) / kPfBlock : 0;
+    const int32_t mask_from = p.causal ? max(0, min(p.kv_len, p.kv_len - p.q_len + t0 + 1)) : p.kv_len;
+
+    __shared__ PrefillLds lds;
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k + (int64_t)g * p.k_head_stride);
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v + (int64_t)g * p.v_head_stride);
+    const uint32_t k0 = pf_lds_addr(&lds.k[0][0]);
+    const uint32_t v0 = pf_lds_addr(&lds.v[0][0]);
+    const float c = p.c;
+
+    float4v o[RT][16];
+    float m_ref[RT], l_run[RT];
+
+    // Up to three passes over the key blocks, one loop body: pass 0 accumulates against each
+    // row's fixed reference (set on its first visible block). If some row of the workgroup
+    // exceeded its reference by more than the slack, pass 1 computes only S and takes each
+    // row's exact scaled maximum as its reference, and pass 2 accumulates again from zero
+    // (it cannot exceed those maxima).
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        m_ref[rt] = -INFINITY;
+        l_run[rt] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[rt][j] = float4v{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int pass_no = 0; pass_no < 3; ++pass_no) {
+        const bool max_only = pass_no == 1;                    // workgroup-uniform
+        // The key loop has no early exit and always updates O (a pass whose result is dropped
+        // still runs to its end): a loop exit that skips the O update keeps the compiler from
+        // accumulating in place.
+        bool over = false;
+        if (nblk > 0) pf_issue_block(p, kbase, vbase, 0, k0, v0, wave, lane);
+        if (nblk > 1) pf_issue_block(p, kbase, vbase, 1, k0 + kPfStageBytes, v0 + kPfStageBytes, wave, lane);
+        for (int32_t blk = 0; blk < nblk; ++blk) {
+            pf_wait_block(blk + 1 < nblk);                    // this wave's loads of block blk
+            __syncthreads();                                  // everyone's have; block blk-1 is done
+            const int st = blk % kPfStages;
+            if (blk + 2 < nblk) {
+                const int sn = (blk + 2) % kPfStages;
+                pf_issue_block(p, kbase, vbase, blk + 2, k0 + sn * kPfStageBytes, v0 + sn * kPfStageBytes, wave,
+                               lane);
+            }
+            const uint8_t* kst = &lds.k[st][0];
+            const uint8_t* vst = &lds.v[st][0];
+            const int32_t key0 = blk * kPfBlock;
+
+            float4v sacc[2][RT];
+#pragma unroll
+            for (int gr = 0; gr < 2; ++gr)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) sacc[gr][rt] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+                for (int gr = 0; gr < 2; ++gr) {
+                    const int row = 16 * gr + n;
+                    const int chunk = (4 * ks + qd) ^ (row & 15);
+                    const half8 a = *reinterpret_cast<const half8*>(kst + row * kPfRowBytes + chunk * 16);
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+                        sacc[gr][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qop[rt][ks], sacc[gr][rt], 0, 0, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+
+            // Lane (n, qd) holds keys key0 + 16*gr + 4*qd + i of its row.
+            const bool need_mask = key0 + kPfBlock > mask_from;
+            half8 pop[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int gr = 0; gr < 2; ++gr)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float x = sacc[gr][rt][i];
+                        if (need_mask) x = (key0 + 16 * gr + 4 * qd + i) < lim[rt] ? x : -INFINITY;
+                        sacc[gr][rt][i] = x;
+                        mx = fmaxf(mx, x);
+                    }
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float ms = mx * c;
+                if (max_only) {
+                    m_ref[rt] = fmaxf(m_ref[rt], ms);
+                } else {
+                    if (m_ref[rt] == -INFINITY) m_ref[rt] = ms;     // the row's first visible block
+                    over |= ms > m_ref[rt] + kPfSlack;
+                }
+#pragma unroll
+                for (int gr = 0; gr < 2; ++gr)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float x = sacc[gr][rt][i];
+                        const float e =
+                            x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -m_ref[rt]));
+                        l_run[rt] += e;
+                        pop[rt][4 * gr + i] = (_Float16)e;
+                    }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+
+            // O^T += V^T . P^T over the block's keys in the order 4*qd + e (e < 4) of granule 0,
+            // then 16 + 4*qd + e - 4 (e >= 4), as P holds them.
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                u32x4 tv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int row = 16 * (e >> 2) + 4 * qd + (e & 3);
+                    const int chunk = (16 * hf + n) ^ (row & 15);
+                    tv[e] = *reinterpret_cast<const u32x4*>(vst + row * kPfRowBytes + chunk * 16);
+                }
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const uint32_t sel = h ? 0x07060302u : 0x05040100u;
+                        u32x4 a;
+#pragma unroll
+                        for (int pp = 0; pp < 4; ++pp) a[pp] = __builtin_amdgcn_perm(tv[2 * pp + 1][w], tv[2 * pp][w], sel);
+                        const half8 ah = __builtin_bit_cast(half8, a);
+                        const int jd = 8 * hf + 2 * w + h;
+#pragma unroll
+                        for (int rt = 0; rt < RT; ++rt)
+                            o[rt][jd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, pop[rt], o[rt][jd], 0, 0, 0);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // no load may still write the ring
+        const bool redo = __syncthreads_or(over) != 0;          // also frees the ring for a next pass
+        if (pass_no == 0 && !redo) break;                       // the common case: one pass
+        if (pass_no == 1) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                l_run[rt] = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) o[rt][j] = float4v{0.f, 0.f, 0.f, 0.f};
+            }
+        } else if (pass_no == 0) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) m_ref[rt] = -INFINITY;
+        }
+    }
+
+    // Normalise and store: O^T tile j element i of lane (n, qd) is dim 8*(4*qd + i) + j (j < 8)
+    // or 128 + 8*(4*qd + i) + j - 8 (j >= 8) of the lane's row.
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        float l = l_run[rt];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        if (tok[rt] >= p.q_len) continue;
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        uint16_t* orow = p.out + (int64_t)tok[rt] * p.o_token_stride + (int64_t)head[rt] * p.o_head_stride;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                half8 v;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = l > 0.0f ? (_Float16)(o[rt][8 * hf + u][i] * inv) : (_Float16)0.0f;
+                *reinterpret_cast<half8*>(orow + 128 * hf + 8 * (4 * qd + i)) = v;
+            }
+    }
+}
+
+}  // namespace
+}  // namespace attn
+
+attn_status attn_launch_prefill(const attn::PrefillParams& p, void* stream) {
+    attn::PrefillParams args = p;
+    void* kargs[] = {&args};
+    const unsigned q_tiles = (unsigned)((p.q_len + p.tokens_per_wg - 1) / p.tokens_per_wg);
+    const unsigned grid = q_tiles * (unsigned)p.num_kv_heads;
+    if (grid == 0) return ATTN_OK;
+    hipError_t e = hipLaunchKernel((const void*)attn::prefill_kernel, dim3(grid), dim3(64 * attn::kPfWaves), kargs, 0,
+                                   (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+// ---- C ABI ----
+
+extern "C" ATTN_API attn_status attn_prefill(const attn_prefill_desc* d, const void* q, const void* k, const void* v,
+                                             void* out, void* stream) {
+    if (!d || !q || !k || !v || !out) return ATTN_E_INVALID;
+    if (d->abi_version != ATTN_ABI_VERSION) return ATTN_E_INVALID;
+    if (d->q_len < 1 || d->kv_len < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1) return ATTN_E_INVALID;
+    if (d->num_q_heads % d->num_kv_heads != 0) return ATTN_E_INVALID;
+    if (d->causal != 0 && d->causal != 1) return ATTN_E_INVALID;
+    if (!(d->sm_scale >= 0.0f) || d->sm_scale > 3.0e38f) return ATTN_E_INVALID;   // NaN, negative, inf
+    const int64_t strides[8] = {d->q_token_stride, d->q_head_stride, d->k_token_stride, d->k_head_stride,
+                                d->v_token_stride, d->v_head_stride, d->o_token_stride, d->o_head_stride};
+    for (int64_t s : strides)
+        if (s < 0 || s % 8 != 0) return ATTN_E_INVALID;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 16 != 0) return ATTN_E_INVALID;
+    // Per-lane 32-bit offsets address one 64-key block from its first key.
+    if (64 * (d->k_token_stride * 2) + 1024 > INT32_MAX || 64 * (d->v_token_stride * 2) + 1024 > INT32_MAX)
+        return ATTN_E_INVALID;
+    const int group = d->num_q_heads / d->num_kv_heads;
+    if (d->head_dim != 256 || 12 % group != 0) return ATTN_E_UNSUPPORTED;
+
+    attn::PrefillParams p{};
+    p.q = (const uint16_t*)q;
+    p.k = (const uint16_t*)k;
+    p.v = (const uint16_t*)v;
+    p.out = (uint16_t*)out;
+    p.q_token_stride = d->q_token_stride;
+    p.q_head_stride = d->q_head_stride;
+    p.k_token_stride = d->k_token_stride;
+    p.k_head_stride = d->k_head_stride;
+    p.v_token_stride = d->v_token_stride;
+    p.v_head_stride = d->v_head_stride;
+    p.o_token_stride = d->o_token_stride;
+    p.o_head_stride = d->o_head_stride;
+    p.q_len = d->q_len;
+    p.kv_len = d->kv_len;
+    p.num_q_heads = d->num_q_heads;
+    p.num_kv_heads = d->num_kv_heads;
+    p.group = group;
+    p.tokens_per_wg = 16 * (12 / group);
+    p.causal = d->causal;
+    const float sm = d->sm_scale > 0.0f ? d->sm_scale : 1.0f / sqrtf((float)d->head_dim);
+    p.c = fmaxf(sm * 1.4426950408889634f, 1.17549435e-38f);
+    return attn_launch_prefill(p, stream);
+}

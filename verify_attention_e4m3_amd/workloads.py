@@ -235,3 +235,50 @@ def host_subset(case: dict, pairs) -> dict:
 def kv_bytes(seq_lens: Sequence[int], num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
     """Algorithmic KV bytes of one layer: every visible token's K and V row read once per KV head."""
     return int(sum(max(0, int(L)) for L in seq_lens)) * num_kv_heads * head_dim * 2 * elem_bytes
+
+
+# ---- long prefill ----
+
+@dataclasses.dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    q_len: int                      # query chunk: the last q_len positions of the sequence
+    kv_len: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    seed: int
+    description: str
+
+
+PREFILL_WORKLOADS = {
+    w.name: w for w in [
+        # The pages' long-prefill operator shapes: Q8192 against KV262144, six query heads per KV
+        # head, at the TP4 / TP2 / TP1 local head counts.
+        PrefillWorkload("prefill_q8192_kv262144_hkv1", 8192, 262144, 6, 1, 256, 9,
+                        "Q8192 x KV262144, Hq6/Hkv1 (TP4 local), FP16 N(0,1) Q/K/V, causal"),
+        PrefillWorkload("prefill_q8192_kv262144_hkv2", 8192, 262144, 12, 2, 256, 10,
+                        "Q8192 x KV262144, Hq12/Hkv2 (TP2 local), FP16 N(0,1) Q/K/V, causal"),
+        PrefillWorkload("prefill_q8192_kv262144_hkv4", 8192, 262144, 24, 4, 256, 11,
+                        "Q8192 x KV262144, Hq24/Hkv4 (TP1 local), FP16 N(0,1) Q/K/V, causal"),
+    ]
+}
+
+
+def prefill_case(*, q_len: int, kv_len: int, num_q_heads: int, num_kv_heads: int, head_dim: int = 256,
+                 seed: int = 0, device="cpu", std: float = 1.0) -> dict:
+    """Seeded FP16 N(0, std^2) q [q_len][Hq][D], k / v [kv_len][Hkv][D]."""
+    g = _gen(seed, device)
+    q = torch.randn((q_len, num_q_heads, head_dim), generator=g, device=device) * std
+    k = torch.randn((kv_len, num_kv_heads, head_dim), generator=g, device=device) * std
+    v = torch.randn((kv_len, num_kv_heads, head_dim), generator=g, device=device) * std
+    return dict(q=q.to(torch.float16), k=k.to(torch.float16), v=v.to(torch.float16))
+
+
+def prefill_flops(q_len: int, kv_len: int, num_q_heads: int, head_dim: int, causal: bool = True) -> int:
+    """Logical (causal) flops: 4 * D per visible (query, key) pair and query head."""
+    if causal:
+        pairs = sum(max(0, min(kv_len, kv_len - q_len + t + 1)) for t in range(q_len))
+    else:
+        pairs = q_len * kv_len
+    return 4 * head_dim * num_q_heads * pairs
