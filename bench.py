@@ -9,7 +9,9 @@ replay: "DFlash2 concurrent long-context attention", section "Attention-only mea
 
 Prints one JSON line: KV read GB/s (whole job), ms per layer, the roofline of the split kernel
 (HBM bytes it must read / its event-timed duration vs 8 TB/s), and the FP64 CPU oracle timed
-on a bounded sample of the same workload.
+on a bounded sample of the same workload. With a long-prefill workload (--workload
+prefill_q8192_kv262144_hkv{1,2,4}) a step is one attn_prefill call and the line reports logical
+causal TFLOP/s against the FP16 MFMA peak instead.
 """
 import argparse
 import hashlib
@@ -108,6 +110,80 @@ def cpu_baseline(w, case, budget_s: float = 15.0):
             "ms_per_layer_extrapolated": round(t_total / len(done) * len(pairs_all) * 1e3, 1)}
 
 
+FP16_MFMA_PEAK_TFLOPS = 2500.0
+PREFILL_METRIC = "prefill logical causal TFLOP/s, Q8192 x KV262144 D256 GQA6, FP16 in, FP32 accumulation"
+
+
+def prefill_cpu_baseline(w, c, budget_s: float = 15.0):
+    """The FP64 oracle on single query tokens of the prefill (each against the keys it sees)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    qn, kn, vn = c["q"].cpu().numpy(), c["k"].cpu().numpy()[None], c["v"].cpu().numpy()[None]
+    table = np.zeros((1, 1), dtype=np.int32)
+    flops, t_total, done = 0, 0.0, 0
+    for t in range(w.q_len - 1, -1, -997):
+        L = w.kv_len - (w.q_len - 1 - t)
+        t1 = time.perf_counter()
+        oracle.verify_attention(qn[t][None, None], kn, vn, table, np.array([L], np.int32), 1.0, 1.0,
+                                page_size=w.kv_len, kv_format="fp16")
+        t_total += time.perf_counter() - t1
+        flops += 4 * w.head_dim * w.num_q_heads * L
+        done += 1
+        if t_total > budget_s:
+            break
+    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} query tokens x {w.num_q_heads} heads, each against its visible keys, FP64 NumPy, "
+                      f"{t_total:.1f} s"}
+
+
+def bench_prefill(args, torch, A, wl):
+    """K timed attn_prefill calls on one Q8192 x KV262144 shape (a step = one call)."""
+    w = wl.PREFILL_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    c = wl.prefill_case(q_len=w.q_len, kv_len=w.kv_len, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                        head_dim=w.head_dim, seed=w.seed, device=dev)
+    out = torch.empty_like(c["q"])
+    flops = wl.prefill_flops(w.q_len, w.kv_len, w.num_q_heads, w.head_dim)
+    steps = args.steps if args.steps_given else 10
+    warmup = args.warmup if args.warmup_given else 3
+    for _ in range(warmup):
+        A.prefill(c["q"], c["k"], c["v"], out=out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        A.prefill(c["q"], c["k"], c["v"], out=out)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for s_, e_ in ev:
+        s_.record(stream)
+        A.prefill(c["q"], c["k"], c["v"], out=out)
+        e_.record(stream)
+    torch.cuda.synchronize()
+    kms = statistics.fmean(s_.elapsed_time(e_) for s_, e_ in ev)
+    achieved = flops / (kms * 1e-3) / 1e12
+    res = {
+        "metric": PREFILL_METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
+        "config": {"workload": w.name, "q_len": w.q_len, "kv_len": w.kv_len, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "causal": True,
+                   "logical_flops_per_call": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_kernel", "kernel_ms_mean": round(kms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = prefill_cpu_baseline(w, c)
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +195,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     args = ap.parse_args()
+    args.steps_given = any(a.startswith("--steps") for a in sys.argv[1:])
+    args.warmup_given = any(a.startswith("--warmup") for a in sys.argv[1:])
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path has no cross-GPU step (each GPU runs its own share "
               "of requests / KV heads); run with --gpus 1", file=sys.stderr)
@@ -128,13 +206,15 @@ def main():
     from verify_attention_e4m3_amd import attention as A
     from verify_attention_e4m3_amd import workloads as wl
 
-    w = wl.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     # All work goes to a stream of its own, as in a serving loop: torch's default stream is
     # HIP's null stream, whose implicit synchronisation with other streams costs several µs
     # per launch.
     torch.cuda.set_stream(torch.cuda.Stream(dev))
+    if args.workload in wl.PREFILL_WORKLOADS:
+        return bench_prefill(args, torch, A, wl)
+    w = wl.WORKLOADS[args.workload]
     layers = [wl.workload_case(w, device=dev, layer=i) for i in range(w.layers)]
     c0 = layers[0]
     plan = A.Plan(q_len=w.q_len, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,

@@ -181,7 +181,8 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
         bool over = false;
         if (nblk > 0) pf_issue_block(p, kbase, vbase, 0, k0, v0, wave, lane);
         if (nblk > 1) pf_issue_block(p, kbase, vbase, 1, k0 + kPfStageBytes, v0 + kPfStageBytes, wave, lane);
-        for (int32_t blk = 0; blk < nblk; ++blk) {
+        auto block = [&](int32_t blk, auto masked_tag) {
+            constexpr bool kMasked = decltype(masked_tag)::value;
             pf_wait_block(blk + 1 < nblk);                    // this wave's loads of block blk
             __syncthreads();                                  // everyone's have; block blk-1 is done
             const int st = blk % kPfStages;
@@ -211,10 +212,8 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
                         sacc[gr][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qop[rt][ks], sacc[gr][rt], 0, 0, 0);
                 }
             }
-            __builtin_amdgcn_sched_barrier(0);
 
             // Lane (n, qd) holds keys key0 + 16*gr + 4*qd + i of its row.
-            const bool need_mask = key0 + kPfBlock > mask_from;
             half8 pop[RT];
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
@@ -224,7 +223,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         float x = sacc[gr][rt][i];
-                        if (need_mask) x = (key0 + 16 * gr + 4 * qd + i) < lim[rt] ? x : -INFINITY;
+                        if constexpr (kMasked) x = (key0 + 16 * gr + 4 * qd + i) < lim[rt] ? x : -INFINITY;
                         sacc[gr][rt][i] = x;
                         mx = fmaxf(mx, x);
                     }
@@ -242,13 +241,14 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const float x = sacc[gr][rt][i];
-                        const float e =
-                            x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -m_ref[rt]));
+                        // unmasked blocks hold finite scores only, and every row has a reference
+                        const float e = (kMasked && x == -INFINITY)
+                                            ? 0.0f
+                                            : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -m_ref[rt]));
                         l_run[rt] += e;
                         pop[rt][4 * gr + i] = (_Float16)e;
                     }
             }
-            __builtin_amdgcn_sched_barrier(0);
 
             // O^T += V^T . P^T over the block's keys in the order 4*qd + e (e < 4) of granule 0,
             // then 16 + 4*qd + e - 4 (e >= 4), as P holds them.
@@ -276,9 +276,14 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
                             o[rt][jd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, pop[rt], o[rt][jd], 0, 0, 0);
                     }
                 }
-                __builtin_amdgcn_sched_barrier(0);
+                
             }
-        }
+        };
+        // Blocks that end at or below every row's visible limit need no mask; the rest (the causal
+        // tail and the ragged end of the keys) run the masked copy of the block body.
+        const int32_t nfull = min(nblk, mask_from / kPfBlock);
+        for (int32_t blk = 0; blk < nfull; ++blk) block(blk, std::false_type{});
+        for (int32_t blk = nfull; blk < nblk; ++blk) block(blk, std::true_type{});
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // no load may still write the ring
         const bool redo = __syncthreads_or(over) != 0;          // also frees the ring for a next pass
         if (pass_no == 0 && !redo) break;                       // the common case: one pass
