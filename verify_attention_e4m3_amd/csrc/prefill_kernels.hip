@@ -13,9 +13,11 @@
 //  * A workgroup of 4 waves (one per SIMD) owns 12 row tiles of 16 query rows: 16 consecutive
 //    tokens of one query head each, all heads of one KV head group, so every K/V byte brought
 //    into LDS serves 192 query rows. Wave w owns row tiles 3w .. 3w+2.
-//  * Keys stream in blocks of 32 through a three-stage LDS ring (K and V, 16 KB each per
-//    stage): right after the one barrier of block b all four waves issue direct global -> LDS
-//    loads of block b+2, so two blocks are in flight during block b's math. 16-byte chunks of a
+//  * Keys stream in blocks of 32 through a four-stage LDS ring (K and V, 16 KB each per stage):
+//    right after the one barrier of an iteration all four waves issue direct global -> LDS loads
+//    three blocks ahead. The loop is software-pipelined: iteration b computes S of block b+1,
+//    whose MFMAs do not depend on (and so overlap) the softmax VALU work of block b, then block
+//    b's softmax and PV. 16-byte chunks of a
 //    token row are XOR-swizzled by token (chunk ^ token % 16), so the MFMA-order LDS reads of 16
 //    lanes hit 16 different bank groups for both K and V.
 //  * S^T = K . Q^T and O^T += V^T . P^T on v_mfma_f32_16x16x32_f16 with the query rows on the
@@ -48,7 +50,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kPfWaves = 4;
 constexpr int kPfRowTilesPerWave = 3;
 constexpr int kPfBlock = 32;                                 // keys per block: two granules of 16
-constexpr int kPfStages = 3;
+constexpr int kPfStages = 4;
 constexpr int kPfD = 256;
 constexpr int kPfRowBytes = kPfD * 2;                        // one token row of one head
 constexpr int kPfStageBytes = kPfBlock * kPfRowBytes;        // 16 KB: one K (or V) block
@@ -99,8 +101,10 @@ __device__ __forceinline__ void pf_issue_block(const PrefillParams& p, const uin
     }
 }
 
-__device__ __forceinline__ void pf_wait_block(bool next_in_flight) {
-    if (next_in_flight) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // block b+1's 8 loads may remain
+// Wait until at most `blocks` newer blocks' loads (8 per wave and block) are still in flight.
+__device__ __forceinline__ void pf_wait_loads(int blocks) {
+    if (blocks >= 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (blocks == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
@@ -179,23 +183,18 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
         // still runs to its end): a loop exit that skips the O update keeps the compiler from
         // accumulating in place.
         bool over = false;
-        if (nblk > 0) pf_issue_block(p, kbase, vbase, 0, k0, v0, wave, lane);
-        if (nblk > 1) pf_issue_block(p, kbase, vbase, 1, k0 + kPfStageBytes, v0 + kPfStageBytes, wave, lane);
-        auto block = [&](int32_t blk, auto masked_tag) {
-            constexpr bool kMasked = decltype(masked_tag)::value;
-            pf_wait_block(blk + 1 < nblk);                    // this wave's loads of block blk
-            __syncthreads();                                  // everyone's have; block blk-1 is done
-            const int st = blk % kPfStages;
-            if (blk + 2 < nblk) {
-                const int sn = (blk + 2) % kPfStages;
-                pf_issue_block(p, kbase, vbase, blk + 2, k0 + sn * kPfStageBytes, v0 + sn * kPfStageBytes, wave,
-                               lane);
-            }
-            const uint8_t* kst = &lds.k[st][0];
-            const uint8_t* vst = &lds.v[st][0];
-            const int32_t key0 = blk * kPfBlock;
-
-            float4v sacc[2][RT];
+        // Software pipeline over the blocks: iteration b computes S of block b+1 (its MFMAs are
+        // independent of, and so overlap, the softmax VALU work of block b), then the softmax and
+        // PV of block b. Block i lives in ring stage i % 4; at iteration b the ring holds K of
+        // b+1, V of b, block b+2 in flight and the stage of b+3 being loaded.
+        auto stage_k = [&](int32_t blk) { return &lds.k[blk % kPfStages][0]; };
+        auto stage_v = [&](int32_t blk) { return &lds.v[blk % kPfStages][0]; };
+        auto issue = [&](int32_t blk) {
+            const int sn = blk % kPfStages;
+            pf_issue_block(p, kbase, vbase, blk, k0 + sn * kPfStageBytes, v0 + sn * kPfStageBytes, wave, lane);
+        };
+        auto qk = [&](int32_t blk, float4v (&sacc)[2][RT]) {
+            const uint8_t* kst = stage_k(blk);
 #pragma unroll
             for (int gr = 0; gr < 2; ++gr)
 #pragma unroll
@@ -212,7 +211,10 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
                         sacc[gr][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qop[rt][ks], sacc[gr][rt], 0, 0, 0);
                 }
             }
-
+        };
+        auto soft_pv = [&](int32_t blk, float4v (&sacc)[2][RT], auto masked_tag) {
+            constexpr bool kMasked = decltype(masked_tag)::value;
+            const int32_t key0 = blk * kPfBlock;
             // Lane (n, qd) holds keys key0 + 16*gr + 4*qd + i of its row.
             half8 pop[RT];
 #pragma unroll
@@ -230,12 +232,12 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
                 mx = fmaxf(mx, __shfl_xor(mx, 16));
                 mx = fmaxf(mx, __shfl_xor(mx, 32));
                 const float ms = mx * c;
-                if (max_only) {
-                    m_ref[rt] = fmaxf(m_ref[rt], ms);
-                } else {
-                    if (m_ref[rt] == -INFINITY) m_ref[rt] = ms;     // the row's first visible block
-                    over |= ms > m_ref[rt] + kPfSlack;
-                }
+                // Branch-free, so that the whole iteration is one scheduling region: the max pass
+                // keeps the running maximum, the others set a row's reference on its first
+                // visible block and flag any block that exceeds it by more than the slack.
+                const float first = m_ref[rt] == -INFINITY ? ms : m_ref[rt];
+                m_ref[rt] = max_only ? fmaxf(m_ref[rt], ms) : first;
+                over |= !max_only && ms > m_ref[rt] + kPfSlack;
 #pragma unroll
                 for (int gr = 0; gr < 2; ++gr)
 #pragma unroll
@@ -249,9 +251,9 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
                         pop[rt][4 * gr + i] = (_Float16)e;
                     }
             }
-
             // O^T += V^T . P^T over the block's keys in the order 4*qd + e (e < 4) of granule 0,
             // then 16 + 4*qd + e - 4 (e >= 4), as P holds them.
+            const uint8_t* vst = stage_v(blk);
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 u32x4 tv[8];
@@ -276,14 +278,35 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
                             o[rt][jd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, pop[rt], o[rt][jd], 0, 0, 0);
                     }
                 }
-                
             }
         };
+
+        float4v s_cur[2][RT];
+        for (int32_t i = 0; i < min(nblk, kPfStages - 1); ++i) issue(i);
+        if (nblk > 0) {
+            pf_wait_loads(min(nblk, kPfStages - 1) - 1);      // block 0 of this wave has landed
+            __syncthreads();
+            qk(0, s_cur);
+        }
+        auto iteration = [&](int32_t b, auto masked_tag) {
+            // Block b+1 (if any) has landed everywhere, and iteration b-1 is done everywhere, so
+            // the stage of block b-1 = b+3 may be refilled.
+            pf_wait_loads(b + 2 < nblk ? 1 : 0);
+            __syncthreads();
+            if (b + kPfStages - 1 < nblk) issue(b + kPfStages - 1);
+            float4v s_next[2][RT];
+            qk(b + 1 < nblk ? b + 1 : b, s_next);             // past the end: a discarded re-read
+            soft_pv(b, s_cur, masked_tag);
+#pragma unroll
+            for (int gr = 0; gr < 2; ++gr)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) s_cur[gr][rt] = s_next[gr][rt];
+        };
         // Blocks that end at or below every row's visible limit need no mask; the rest (the causal
-        // tail and the ragged end of the keys) run the masked copy of the block body.
+        // tail and the ragged end of the keys) run the masked copy of the softmax.
         const int32_t nfull = min(nblk, mask_from / kPfBlock);
-        for (int32_t blk = 0; blk < nfull; ++blk) block(blk, std::false_type{});
-        for (int32_t blk = nfull; blk < nblk; ++blk) block(blk, std::true_type{});
+        for (int32_t b = 0; b < nfull; ++b) iteration(b, std::false_type{});
+        for (int32_t b = nfull; b < nblk; ++b) iteration(b, std::true_type{});
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // no load may still write the ring
         const bool redo = __syncthreads_or(over) != 0;          // also frees the ring for a next pass
         if (pass_no == 0 && !redo) break;                       // the common case: one pass
