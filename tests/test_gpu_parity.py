@@ -179,8 +179,37 @@ def test_fp16_values_pass_through_exactly():
         assert torch.equal(out[0, 0, h], want), h
 
 
+FP16_D256 = [
+    dict(batch=2, seq_lens=[5, 700], q_len=8, num_q_heads=6, num_kv_heads=1, page_size=16),
+    dict(batch=3, seq_lens=[3000, 33, 0], q_len=8, num_q_heads=24, num_kv_heads=4, page_size=1648),
+    dict(batch=2, seq_lens=[9000, 17], q_len=1, num_q_heads=8, num_kv_heads=2, page_size=32),
+    dict(batch=2, seq_lens=[1025, 64], q_len=4, num_q_heads=16, num_kv_heads=4, page_size=48),
+]
+
+
+@pytest.mark.parametrize("kw", FP16_D256, ids=lambda kw: f"fp16d256-B{kw['batch']}-L{max(kw['seq_lens'])}-q{kw['q_len']}-"
+                                                           f"H{kw['num_q_heads']}/{kw['num_kv_heads']}")
+def test_parity_fp16_d256(kw):
+    note(f"parity fp16 d256 {kw}")
+    c = _case(head_dim=256, kv_format="fp16", seed=sum(kw["seq_lens"]) + 11, **kw)
+    compare(run_gpu(c), run_oracle(c))
+
+
+def test_fp16_d256_values_pass_through_exactly():
+    # L == q_len: verify token 0 sees only key 0, so its output is that V row exactly.
+    note("fp16 d256 identity row")
+    c = _case(batch=1, seq_lens=[8], q_len=8, num_q_heads=6, num_kv_heads=1, head_dim=256, page_size=16,
+              kv_format="fp16", seed=12)
+    out = run_gpu(c)
+    page = int(c["block_table"][0, 0])
+    want = c["v_cache"][page, 0, 0, :]
+    for h in range(6):
+        assert torch.equal(out[0, 0, h], want), h
+
+
 @pytest.mark.parametrize("name", ["verify_b1_ctx3297_hq6_hkv1", "verify_b4_ctx32k_gqa6",
-                                  "decode_b8_ctx32k_d128_fp16_gqa4", "verify_b4_ctx32k_gqa6_e5m2"])
+                                  "decode_b8_ctx32k_d128_fp16_gqa4", "verify_b4_ctx32k_gqa6_e5m2",
+                                  "verify_b4_ctx32k_gqa6_fp16_d256"])
 def test_parity_workload_full(name):
     note(f"parity full workload {name}")
     w = wl.WORKLOADS[name]

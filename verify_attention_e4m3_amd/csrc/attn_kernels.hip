@@ -41,6 +41,7 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -78,10 +79,13 @@ constexpr int kMaxSplitPages = 32768 / 16 + 2;
 struct TileK { u32x4 k[2][4]; };
 struct TileV { u32x4 v[8]; };
 
-// KV element formats whose token rows of one head are 256 bytes: E4M3 and E5M2 at D = 256 and
-// FP16 at D = 128. They share the gather, the LDS ring and the swizzle; they differ in how a
-// lane's 16 bytes become MFMA operands and which output dims an accumulator element holds.
-enum KvFormat { kFmtE4M3D256 = 0, kFmtF16D128 = 1, kFmtE5M2D256 = 2 };
+// KV element formats. A tile is two granules of 16 rows of 256 bytes: for E4M3 / E5M2 at D = 256
+// and FP16 at D = 128 (256-byte token rows) they are 32 consecutive tokens; for FP16 at D = 256
+// (512-byte rows) they are the two 256-byte halves of 16 tokens. All share the gather, the LDS
+// ring and the swizzle; they differ in how a lane's 16 bytes become MFMA operands and which
+// output dims an accumulator element holds. Traits: TILE tokens per tile, NG granules of scores
+// per tile, B_TOK / B_BYTES the token and byte offset of granule B from granule A.
+enum KvFormat { kFmtE4M3D256 = 0, kFmtF16D128 = 1, kFmtE5M2D256 = 2, kFmtF16D256 = 3 };
 
 // Byte -> FP16 decoders of the one-byte formats; both are exact.
 // E4M3: v_cvt_scalef32_pk_f16_fp8 with scale 1.0 (every finite E4M3 value is an FP16 value).
@@ -113,11 +117,37 @@ struct DecE5M2 {
 
 // One-byte formats, D = 256. K vector i of a lane holds dims 64*i + 16*qd + 0..15 (one byte
 // each) and feeds k-steps 2i and 2i+1; PV MFMA j (0..15) covers dims 16*m + j.
+// S^T = K . Q^T for the two 16-token granules of a 32-token tile (one accumulator each).
+template <class F, int RT>
+__device__ __forceinline__ void qk_two_granules(const TileK& t, float4v (&sacc)[2][RT],
+                                                const half8 (&qop)[RT][F::KSTEPS]) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) sacc[tt][rt] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < F::KSTEPS; ++ks) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const half8 a = F::k_op(t.k[tt], ks);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                sacc[tt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qop[rt][ks], sacc[tt][rt], 0, 0, 0);
+        }
+    }
+}
+
 template <class Dec>
 struct Fmt8D256 {
     static constexpr int D = 256;
     static constexpr int KSTEPS = 8;
     static constexpr int JT = 16;
+    static constexpr int TILE = 32, NG = 2, B_TOK = 16, B_BYTES = 0;
+    typedef half8 PopT;
+    template <int RT>
+    __device__ static void qk(const TileK& t, float4v (&sacc)[2][RT], const half8 (&qop)[RT][KSTEPS]) {
+        qk_two_granules<Fmt8D256, RT>(t, sacc, qop);
+    }
     __device__ static int q_dim(int ks, int qd) { return 64 * (ks >> 1) + 16 * qd + 8 * (ks & 1); }
     __device__ static half8 k_op(const u32x4 (&k)[4], int ks) {
         const u32x4 w = k[ks >> 1];
@@ -163,6 +193,12 @@ template <> struct Fmt<kFmtF16D128> {
     static constexpr int D = 128;
     static constexpr int KSTEPS = 4;
     static constexpr int JT = 8;
+    static constexpr int TILE = 32, NG = 2, B_TOK = 16, B_BYTES = 0;
+    typedef half8 PopT;
+    template <int RT>
+    __device__ static void qk(const TileK& t, float4v (&sacc)[2][RT], const half8 (&qop)[RT][KSTEPS]) {
+        qk_two_granules<Fmt<kFmtF16D128>, RT>(t, sacc, qop);
+    }
     __device__ static int q_dim(int ks, int qd) { return 32 * ks + 8 * qd; }
     __device__ static half8 k_op(const u32x4 (&k)[4], int ks) { return __builtin_bit_cast(half8, k[ks]); }
     __device__ static int o_dim(int qd, int i, int j) { return 8 * (4 * qd + i) + j; }
@@ -185,6 +221,54 @@ template <> struct Fmt<kFmtF16D128> {
                     o[rt][jd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, pop[rt], o[rt][jd], 0, 0, 0);
             }
         }
+    }
+};
+
+// FP16, D = 256: 512-byte token rows, so a tile is 16 tokens and its granules A and B are their
+// dims 0..127 and 128..255 (granule B = same tokens, 256 bytes on). K vector i of granule tt of
+// a lane holds dims 128*tt + 32*i + 8*qd + 0..7 (k-step 4*tt + i as it is); both halves
+// accumulate into one score tile. PV runs on v_mfma_f32_16x16x16_f16 over the 16 tokens: lane
+// (m, qd) holds dims 8m..8m+7 (slots 0..3) and 128+8m.. (slots 4..7) of tokens 4*qd + 0..3, and
+// MFMA j covers dims 8m + j (j < 8) or 128 + 8m + j - 8.
+template <> struct Fmt<kFmtF16D256> {
+    static constexpr int D = 256;
+    static constexpr int KSTEPS = 8;
+    static constexpr int JT = 16;
+    static constexpr int TILE = 16, NG = 1, B_TOK = 0, B_BYTES = 256;
+    typedef half4 PopT;
+    __device__ static int q_dim(int ks, int qd) { return 32 * ks + 8 * qd; }
+    __device__ static int o_dim(int qd, int i, int j) { return j < 8 ? 8 * (4 * qd + i) + j : 128 + 8 * (4 * qd + i) + j - 8; }
+    template <int RT>
+    __device__ static void qk(const TileK& t, float4v (&sacc)[2][RT], const half8 (&qop)[RT][KSTEPS]) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) sacc[0][rt] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const half8 a = __builtin_bit_cast(half8, t.k[tt][ks]);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    sacc[0][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qop[rt][4 * tt + ks], sacc[0][rt], 0, 0, 0);
+            }
+    }
+    template <int RT>
+    __device__ static void pv(const TileV& t, const half4 (&pop)[RT], float4v (&o)[RT][JT]) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t sel = h ? 0x07060302u : 0x05040100u;
+                    const uint32_t a0 = __builtin_amdgcn_perm(t.v[4 * hf + 1][w], t.v[4 * hf][w], sel);
+                    const uint32_t a1 = __builtin_amdgcn_perm(t.v[4 * hf + 3][w], t.v[4 * hf + 2][w], sel);
+                    const half4 ah = __builtin_bit_cast(half4, (uint32_t __attribute__((ext_vector_type(2)))){a0, a1});
+                    const int jd = 8 * hf + 2 * w + h;
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+                        o[rt][jd] = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, pop[rt], o[rt][jd], 0, 0, 0);
+                }
     }
 };
 
@@ -233,22 +317,23 @@ struct Granules {
     bool past_end;       // a prefetch beyond the split: every lane re-reads token `last`
 };
 
+template <class F>
 __device__ __forceinline__ Granules granules(int32_t j0, int32_t last, const int32_t* pages, int32_t pg0,
                                              const uint8_t* kbase, const uint8_t* vbase, const RunParams& p) {
     Granules gr;
     gr.past_end = j0 > last;
     if (gr.past_end) j0 = last & ~15;
     gr.j0 = j0;
-    gr.gsB = min(j0 + 16, last & ~15);
+    gr.gsB = min(j0 + F::B_TOK, last & ~15);
     int32_t ia, sa, ib, sb;
     locate(j0, p, ia, sa);
     locate(gr.gsB, p, ib, sb);
     const int64_t pageA = __builtin_amdgcn_readfirstlane(pages[ia - pg0]);
     const int64_t pageB = __builtin_amdgcn_readfirstlane(pages[ib - pg0]);
     gr.kA = kbase + pageA * p.k_page_stride + (int64_t)sa * p.k_token_stride;
-    gr.kB = kbase + pageB * p.k_page_stride + (int64_t)sb * p.k_token_stride;
+    gr.kB = kbase + pageB * p.k_page_stride + (int64_t)sb * p.k_token_stride + F::B_BYTES;
     gr.vA = vbase + pageA * p.v_page_stride + (int64_t)sa * p.v_token_stride;
-    gr.vB = vbase + pageB * p.v_page_stride + (int64_t)sb * p.v_token_stride;
+    gr.vB = vbase + pageB * p.v_page_stride + (int64_t)sb * p.v_token_stride + F::B_BYTES;
     return gr;
 }
 
@@ -278,9 +363,10 @@ constexpr int kStageBytes = kStageRows * 64 * 16;
 // clamps each lane's token to `last` (whose page exists; the extra tokens are masked). A
 // prefetch past the split's end keeps the per-tile load count (so the ring's vmcnt accounting
 // is the same every iteration) but reads only token `last`'s row, which stays in L2.
+template <class F>
 __device__ __forceinline__ void issue_k(const Granules& gr, int32_t last, const LaneOffs& lo, uint32_t stage,
                                         const RunParams& p, int lane) {
-    if (gr.j0 + kTileTokens - 1 <= last && !gr.past_end) {
+    if (gr.j0 + F::TILE - 1 <= last && !gr.past_end) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             dma16(gr.kA, lo.k[i], stage + i * 1024);
@@ -295,7 +381,7 @@ __device__ __forceinline__ void issue_k(const Granules& gr, int32_t last, const 
             const uint32_t oa =
                 (uint32_t)((min(gr.j0 + tok, last) - gr.j0) * p.k_token_stride + 16 * (slot ^ tok));
             const uint32_t ob =
-                (uint32_t)((min(gr.j0 + 16 + tok, last) - gr.gsB) * p.k_token_stride + 16 * (slot ^ tok));
+                (uint32_t)((min(gr.j0 + F::B_TOK + tok, last) - gr.gsB) * p.k_token_stride + 16 * (slot ^ tok));
             dma16(gr.kA, gr.past_end ? (uint32_t)((last - cap) * p.k_token_stride + 16 * slot) : oa, stage + i * 1024);
             dma16(gr.kB, gr.past_end ? (uint32_t)((last - cap) * p.k_token_stride + 16 * slot) : ob,
                   stage + (4 + i) * 1024);
@@ -303,9 +389,10 @@ __device__ __forceinline__ void issue_k(const Granules& gr, int32_t last, const 
     }
 }
 
+template <class F>
 __device__ __forceinline__ void issue_v(const Granules& gr, int32_t last, const LaneOffs& lo, uint32_t stage,
                                         const RunParams& p, int n, int qd) {
-    if (gr.j0 + kTileTokens - 1 <= last && !gr.past_end) {
+    if (gr.j0 + F::TILE - 1 <= last && !gr.past_end) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             dma16(gr.vA, lo.v[e], stage + (8 + e) * 1024);
@@ -316,7 +403,7 @@ __device__ __forceinline__ void issue_v(const Granules& gr, int32_t last, const 
         for (int e = 0; e < 4; ++e) {
             const int rel = 4 * qd + e;
             const uint32_t oa = (uint32_t)((min(gr.j0 + rel, last) - gr.j0) * p.v_token_stride + 16 * n);
-            const uint32_t ob = (uint32_t)((min(gr.j0 + 16 + rel, last) - gr.gsB) * p.v_token_stride + 16 * n);
+            const uint32_t ob = (uint32_t)((min(gr.j0 + F::B_TOK + rel, last) - gr.gsB) * p.v_token_stride + 16 * n);
             const uint32_t oz = (uint32_t)((last - gr.j0) * p.v_token_stride + 16 * n);
             dma16(gr.vA, gr.past_end ? oz : oa, stage + (8 + e) * 1024);
             dma16(gr.vB, gr.past_end ? oz : ob, stage + (12 + e) * 1024);
@@ -330,45 +417,27 @@ __device__ __forceinline__ void vm_wait_oldest_half_tile() { asm volatile("s_wai
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// S^T = K . Q^T for the tile's two 16-token granules and the row tiles.
-template <int FMT, int RT>
-__device__ __forceinline__ void qk_tile(const TileK& t, float4v (&sacc)[2][RT], const half8 (&qop)[RT][Fmt<FMT>::KSTEPS]) {
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) sacc[tt][rt] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < Fmt<FMT>::KSTEPS; ++ks) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const half8 a = Fmt<FMT>::k_op(t.k[tt], ks);
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                sacc[tt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qop[rt][ks], sacc[tt][rt], 0, 0, 0);
-        }
-    }
-}
-
-// Softmax step of one tile: masked raw scores (lane holds row n's tokens j0 + 16*tt + 4*qd + i),
-// exponentials exp2(c*x - m) against the row references (c > 0, log2 units), P^T in FP16.
-// Returns true (uniformly) when a row's tile max exceeds its reference by more than kRefSlack;
-// the references are then raised and nothing was accumulated.
-template <int RT>
+// Softmax step of one tile: masked raw scores (lane holds row n's tokens j0 + 16*tt + 4*qd + i of
+// the NG granules of scores), exponentials exp2(c*x - m) against the row references (c > 0,
+// log2 units), P^T in FP16. Returns true (uniformly) when a row's tile max exceeds its reference
+// by more than kRefSlack; the references are then raised and nothing was accumulated.
+template <int RT, int NG, int TILE, class PopT>
 __device__ __forceinline__ bool softmax_tile(const float4v (&sacc)[2][RT], int32_t j0, int32_t mask_from,
                                              const int32_t (&lim)[RT], float c, float (&m_ref)[RT],
-                                             float (&l_run)[RT], half8 (&pop)[RT], int qd) {
-    float x[RT][8];
+                                             float (&l_run)[RT], PopT (&pop)[RT], int qd) {
+    constexpr int NV = 4 * NG;
+    float x[RT][NV];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < NG; ++tt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) x[rt][tt * 4 + i] = sacc[tt][rt][i];
-    if (j0 + kTileTokens > mask_from) {      // only tiles at the causal tail or the row end
+    if (j0 + TILE > mask_from) {             // only tiles at the causal tail or the row end
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+            for (int tt = 0; tt < NG; ++tt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     x[rt][tt * 4 + i] = (j0 + 16 * tt + 4 * qd + i) < lim[rt] ? x[rt][tt * 4 + i] : -INFINITY;
@@ -377,8 +446,9 @@ __device__ __forceinline__ bool softmax_tile(const float4v (&sacc)[2][RT], int32
     bool over = false;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        float m = max3f(max3f(x[rt][0], x[rt][1], x[rt][2]), max3f(x[rt][3], x[rt][4], x[rt][5]),
-                        max3f(x[rt][6], x[rt][7], x[rt][7]));
+        float m = NG == 2 ? max3f(max3f(x[rt][0], x[rt][1], x[rt][2]), max3f(x[rt][3], x[rt][4 % NV], x[rt][5 % NV]),
+                                  max3f(x[rt][6 % NV], x[rt][7 % NV], x[rt][7 % NV]))
+                          : max3f(max3f(x[rt][0], x[rt][1], x[rt][2]), x[rt][3], x[rt][3]);
         const float m16 = __shfl_xor(m, 16);
         m = max3f(m, m16, m16);
         const float m32 = __shfl_xor(m, 32);
@@ -396,12 +466,14 @@ __device__ __forceinline__ bool softmax_tile(const float4v (&sacc)[2][RT], int32
     for (int rt = 0; rt < RT; ++rt) {
         if (m_ref[rt] == -INFINITY) m_ref[rt] = mx[rt];        // first tile with a visible key
         const float neg_m = m_ref[rt] == -INFINITY ? 0.0f : -m_ref[rt];
-        float pe[8];
+        float pe[NV];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(__builtin_fmaf(x[rt][e], c, neg_m));
-        l_run[rt] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+        for (int e = 0; e < NV; ++e) pe[e] = fast_exp2(__builtin_fmaf(x[rt][e], c, neg_m));
+        float sum = (pe[0] + pe[1]) + (pe[2] + pe[3]);
+        if constexpr (NV == 8) sum += (pe[4 % NV] + pe[5 % NV]) + (pe[6 % NV] + pe[7 % NV]);
+        l_run[rt] += sum;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pop[rt][e] = (_Float16)pe[e];
+        for (int e = 0; e < NV; ++e) pop[rt][e] = (_Float16)pe[e];
     }
     return false;
 }
@@ -413,13 +485,14 @@ __device__ __forceinline__ void split_row_max(float (&m)[RT], int32_t j_begin, i
                                               const int32_t (&lim)[RT], float c, const int32_t* pages, int32_t pg0,
                                               const uint8_t* kbase, const uint8_t* vbase, const RunParams& p,
                                               const half8 (&qop)[RT][Fmt<FMT>::KSTEPS], int n, int qd) {
+    using F = Fmt<FMT>;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) m[rt] = -INFINITY;
     const int32_t last = j_end - 1;
-    for (int32_t j0 = j_begin; j0 < j_end; j0 += kTileTokens) {
-        const Granules gr = granules(j0, last, pages, pg0, kbase, vbase, p);
+    for (int32_t j0 = j_begin; j0 < j_end; j0 += F::TILE) {
+        const Granules gr = granules<F>(j0, last, pages, pg0, kbase, vbase, p);
         const uint8_t* rowA = gr.kA + (int64_t)(min(j0 + n, last) - j0) * p.k_token_stride + 16 * qd;
-        const uint8_t* rowB = gr.kB + (int64_t)(min(j0 + 16 + n, last) - gr.gsB) * p.k_token_stride + 16 * qd;
+        const uint8_t* rowB = gr.kB + (int64_t)(min(j0 + F::B_TOK + n, last) - gr.gsB) * p.k_token_stride + 16 * qd;
         TileK t;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -427,13 +500,13 @@ __device__ __forceinline__ void split_row_max(float (&m)[RT], int32_t j_begin, i
             t.k[1][i] = *reinterpret_cast<const u32x4*>(rowB + 64 * i);
         }
         float4v sacc[2][RT];
-        qk_tile<FMT, RT>(t, sacc, qop);
-        const bool need_mask = j0 + kTileTokens > mask_from;
+        F::template qk<RT>(t, sacc, qop);
+        const bool need_mask = j0 + F::TILE > mask_from;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             float mx = -INFINITY;
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+            for (int tt = 0; tt < F::NG; ++tt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float v = sacc[tt][rt][i];
@@ -573,8 +646,8 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void split_kernel(RunParam
     uint32_t k_rd[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) k_rd[i] = n * 256 + 16 * ((4 * i + qd) ^ n);
-    constexpr int32_t kStride = kWavesPerHead * kTileTokens;    // tokens between a wave's tiles
-    const int32_t first = j_begin + half * kTileTokens;          // this wave's first tile
+    constexpr int32_t kStride = kWavesPerHead * F::TILE;        // tokens between a wave's tiles
+    const int32_t first = j_begin + half * F::TILE;              // this wave's first tile
 
     // Per-row reference max (log2 units). A row's reference is the max of the first tile in
     // which the wave sees a key for it; exponentials are taken against it, so O and l never
@@ -596,19 +669,19 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void split_kernel(RunParam
         }
         if (first > last) return false;          // a short split may leave a second wave no tile
         {
-            const Granules g0 = granules(first, last, pages, pg0, kbase, vbase, p);
-            issue_k(g0, last, lo, ring0, p, lane);
-            issue_v(g0, last, lo, ring0, p, n, qd);
-            const Granules g1 = granules(first + kStride, last, pages, pg0, kbase, vbase, p);
-            issue_k(g1, last, lo, ring0 + kStageBytes, p, lane);
-            issue_v(g1, last, lo, ring0 + kStageBytes, p, n, qd);
+            const Granules g0 = granules<F>(first, last, pages, pg0, kbase, vbase, p);
+            issue_k<F>(g0, last, lo, ring0, p, lane);
+            issue_v<F>(g0, last, lo, ring0, p, n, qd);
+            const Granules g1 = granules<F>(first + kStride, last, pages, pg0, kbase, vbase, p);
+            issue_k<F>(g1, last, lo, ring0 + kStageBytes, p, lane);
+            issue_v<F>(g1, last, lo, ring0 + kStageBytes, p, n, qd);
         }
         bool over = false;
         int32_t j0 = first;
         for (int st = 0;; st ^= 1) {
             const uint32_t stage = ring0 + st * kStageBytes;
             const u32x4* sl = ring_lane + st * (kStageBytes / 16);
-            const Granules gn = granules(j0 + 2 * kStride, last, pages, pg0, kbase, vbase, p);
+            const Granules gn = granules<F>(j0 + 2 * kStride, last, pages, pg0, kbase, vbase, p);
             vm_wait_oldest_half_tile();         // tile k's K has landed
             TileK tk;
             const uint8_t* stage_bytes = ring + st * kStageBytes;
@@ -618,17 +691,17 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void split_kernel(RunParam
                 for (int i = 0; i < 4; ++i)
                     tk.k[tt][i] = *reinterpret_cast<const u32x4*>(stage_bytes + tt * 4096 + k_rd[i]);
             lds_wait_all();
-            issue_k(gn, last, lo, stage, p, lane);
+            issue_k<F>(gn, last, lo, stage, p, lane);
             float4v sacc[2][RT];
-            qk_tile<FMT, RT>(tk, sacc, qop);
-            half8 pop[RT];
-            over = softmax_tile<RT>(sacc, j0, mask_from, lim, c, m_ref, l_run, pop, qd);
+            F::template qk<RT>(tk, sacc, qop);
+            typename F::PopT pop[RT];
+            over = softmax_tile<RT, F::NG, F::TILE>(sacc, j0, mask_from, lim, c, m_ref, l_run, pop, qd);
             TileV tv;
             vm_wait_oldest_half_tile();         // tile k's V has landed
 #pragma unroll
             for (int e = 0; e < 8; ++e) tv.v[e] = sl[(8 + e) * 64];
             lds_wait_all();
-            issue_v(gn, last, lo, stage, p, n, qd);
+            issue_v<F>(gn, last, lo, stage, p, n, qd);
             if (over) break;
             F::template pv<RT>(tv, pop, o);
             j0 += kStride;
@@ -807,9 +880,14 @@ attn_status attn_launch_split(const attn_plan_s* plan, const attn::RunParams& p,
     void* kargs[] = {&args};
     const int row_tiles = p.rows_alloc / 16;
     const int hp = attn::heads_per_workgroup(p.num_kv_heads, p.batch, p.grid_splits, plan->num_cus);
-    attn::KernelFn fn = plan->desc.kv_dtype == ATTN_KV_FP16   ? attn::split_for<attn::kFmtF16D128>(row_tiles, hp)
-                        : plan->desc.kv_dtype == ATTN_KV_E5M2 ? attn::split_for<attn::kFmtE5M2D256>(row_tiles, hp)
-                                                              : attn::split_for<attn::kFmtE4M3D256>(row_tiles, hp);
+    attn::KernelFn fn;
+    if (plan->desc.kv_dtype == ATTN_KV_FP16)
+        fn = plan->desc.head_dim == 256 ? attn::split_for<attn::kFmtF16D256>(row_tiles, hp)
+                                        : attn::split_for<attn::kFmtF16D128>(row_tiles, hp);
+    else if (plan->desc.kv_dtype == ATTN_KV_E5M2)
+        fn = attn::split_for<attn::kFmtE5M2D256>(row_tiles, hp);
+    else
+        fn = attn::split_for<attn::kFmtE4M3D256>(row_tiles, hp);
     // One workgroup per (slot, split, group of hp KV heads); the kernel decodes the same order.
     const unsigned grid = (unsigned)p.batch * (p.num_kv_heads / hp) * p.grid_splits;
     hipError_t e = hipLaunchKernel((const void*)fn, dim3(grid), dim3(64 * attn::kWavesPerHead * hp), kargs, 0,

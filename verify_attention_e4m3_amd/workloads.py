@@ -59,6 +59,11 @@ WORKLOADS = {
                  MAX_SEQ_LEN, "B16, lengths U{0..262144}, two zero-length rows, three padded slots, page 3296"),
         Workload("decode_b8_ctx32k_d128_fp16_gqa4", 8, 32768, 1, 32, 8, 128, 1648, "fp16", 1.0, 1.0, 1, 5,
                  32768, "B8 x 32768, q1, Hq32/Hkv8, D128, FP16 K/V"),
+        # FP16 KV at D256 (another cache format the pages' backend serves)
+        Workload("verify_b4_ctx32k_gqa6_fp16_d256", 4, 32768, 8, 24, 4, 256, 1648, "fp16", 1.0, 1.0, 1, 12, 32768,
+                 "B4 x 32768, Hq24/Hkv4, FP16 KV at D256, shuffled pages"),
+        Workload("verify_b8_ctx128k_gqa6_fp16_d256_4layers", 8, 131072, 8, 24, 4, 256, 1648, "fp16", 1.0, 1.0, 4,
+                 13, 131072, "B8 x 131072, Hq24/Hkv4, FP16 KV at D256 (4.3 GB per layer), 4 per-layer caches"),
         # four local query heads on one KV head (the pages' TP4 geometry of another model), q8
         Workload("verify_b8_ctx128k_hq4_hkv1_16layers", 8, 131072, 8, 4, 1, 256, 1648, "e4m3", 1.0, 1.0, 16, 8,
                  131072, "B8 x 131072, q8, Hq4/Hkv1 (32 packed rows), 16 per-layer caches, shuffled pages"),
