@@ -74,6 +74,7 @@ def test_capabilities():
     assert {"kv_dtype": A.ATTN_KV_FP16, "head_dim": 128, "max_q_len": 8, "max_rows": 48} in caps["geometries"]
     assert {"kv_dtype": A.ATTN_KV_E5M2, "head_dim": 256, "max_q_len": 8, "max_rows": 48} in caps["geometries"]
     assert {"kv_dtype": A.ATTN_KV_FP16, "head_dim": 256, "max_q_len": 8, "max_rows": 48} in caps["geometries"]
+    assert {"kv_dtype": A.ATTN_KV_E4M3, "head_dim": 128, "max_q_len": 8, "max_rows": 48} in caps["geometries"]
 
 
 def test_status_strings():
@@ -109,7 +110,7 @@ def plan(**kw):
     (dict(abi_version=2), A.ATTN_E_INVALID),
     (dict(kv_dtype="e3m4"), A.ATTN_E_INVALID),                         # not a KV dtype of the ABI
     (dict(kv_dtype="e5m2", head_dim=128), A.ATTN_E_UNSUPPORTED),       # E5M2 at D128 is not built
-    (dict(head_dim=128), A.ATTN_E_UNSUPPORTED),                       # E4M3 at D128 is not built
+    (dict(head_dim=64), A.ATTN_E_UNSUPPORTED),                        # E4M3 at D64 is not built
     (dict(kv_dtype="fp16", head_dim=64), A.ATTN_E_UNSUPPORTED),         # FP16 at D64 is not built
     (dict(q_len=9, num_q_heads=4, num_kv_heads=4), A.ATTN_E_UNSUPPORTED),
     (dict(num_q_heads=28), A.ATTN_E_UNSUPPORTED),                       # G = 7 -> 56 rows > 48
@@ -127,6 +128,7 @@ def test_admission_rejects(kw, status):
     dict(kv_dtype="fp16", head_dim=128, q_len=1, num_q_heads=32, num_kv_heads=8),
     dict(kv_dtype="e5m2"),
     dict(kv_dtype="fp16"),                                                 # FP16 at D256
+    dict(head_dim=128),                                                    # E4M3 at D128
 ])
 def test_admission_accepts(kw):
     p = plan(**kw)

@@ -207,9 +207,42 @@ def test_fp16_d256_values_pass_through_exactly():
         assert torch.equal(out[0, 0, h], want), h
 
 
+E4M3_D128 = [
+    dict(batch=2, seq_lens=[5, 700], q_len=8, num_q_heads=6, num_kv_heads=1, page_size=16),
+    dict(batch=3, seq_lens=[3000, 33, 0], q_len=8, num_q_heads=24, num_kv_heads=4, page_size=1648),
+    dict(batch=2, seq_lens=[9000, 17], q_len=1, num_q_heads=8, num_kv_heads=2, page_size=32),
+    dict(batch=2, seq_lens=[1025, 64], q_len=4, num_q_heads=16, num_kv_heads=4, page_size=48),
+]
+
+
+@pytest.mark.parametrize("kw", E4M3_D128, ids=lambda kw: f"e4m3d128-B{kw['batch']}-L{max(kw['seq_lens'])}-q{kw['q_len']}-"
+                                                           f"H{kw['num_q_heads']}/{kw['num_kv_heads']}")
+def test_parity_e4m3_d128(kw):
+    note(f"parity e4m3 d128 {kw}")
+    c = _case(head_dim=128, seed=sum(kw["seq_lens"]) + 13, **kw)
+    compare(run_gpu(c), run_oracle(c))
+
+
+@pytest.mark.parametrize("half", [0, 1])
+def test_e4m3_d128_bytes_decode_exactly(half):
+    # The only visible key's V row (128 dims) holds half of the 254 finite E4M3 values.
+    note(f"e4m3 d128 bytes, half {half}")
+    c = _case(batch=1, seq_lens=[8], q_len=8, num_q_heads=6, num_kv_heads=1, head_dim=128, page_size=16, seed=103)
+    vals = np.arange(128 * half, 128 * half + 128, dtype=np.uint8)
+    vals[(vals == 0x7F) | (vals == 0xFF)] = 0
+    page = int(c["block_table"][0, 0])
+    c["v_cache"][page, 0, 0, :] = torch.from_numpy(vals).cuda()
+    out = run_gpu(c)
+    want = torch.from_numpy(oracle.decode_table()[vals].astype(np.float16)).cuda()
+    for h in range(6):
+        assert torch.equal(out[0, 0, h], want), h
+        nonzero = want != 0
+        assert torch.equal(out[0, 0, h][nonzero].view(torch.int16), want[nonzero].view(torch.int16)), h
+
+
 @pytest.mark.parametrize("name", ["verify_b1_ctx3297_hq6_hkv1", "verify_b4_ctx32k_gqa6",
                                   "decode_b8_ctx32k_d128_fp16_gqa4", "verify_b4_ctx32k_gqa6_e5m2",
-                                  "verify_b4_ctx32k_gqa6_fp16_d256"])
+                                  "verify_b4_ctx32k_gqa6_fp16_d256", "verify_b4_ctx32k_gqa6_e4m3_d128"])
 def test_parity_workload_full(name):
     note(f"parity full workload {name}")
     w = wl.WORKLOADS[name]

@@ -84,8 +84,9 @@ struct TileV { u32x4 v[8]; };
 // (512-byte rows) they are the two 256-byte halves of 16 tokens. All share the gather, the LDS
 // ring and the swizzle; they differ in how a lane's 16 bytes become MFMA operands and which
 // output dims an accumulator element holds. Traits: TILE tokens per tile, NG granules of scores
-// per tile, B_TOK / B_BYTES the token and byte offset of granule B from granule A.
-enum KvFormat { kFmtE4M3D256 = 0, kFmtF16D128 = 1, kFmtE5M2D256 = 2, kFmtF16D256 = 3 };
+// per tile, B_TOK / B_BYTES the token and byte offset of granule B from granule A, ROW the bytes
+// of one head's token row (E4M3 at D = 128 has 128-byte rows: see Fmt<kFmtE4M3D128>).
+enum KvFormat { kFmtE4M3D256 = 0, kFmtF16D128 = 1, kFmtE5M2D256 = 2, kFmtF16D256 = 3, kFmtE4M3D128 = 4 };
 
 // Byte -> FP16 decoders of the one-byte formats; both are exact.
 // E4M3: v_cvt_scalef32_pk_f16_fp8 with scale 1.0 (every finite E4M3 value is an FP16 value).
@@ -142,7 +143,7 @@ struct Fmt8D256 {
     static constexpr int D = 256;
     static constexpr int KSTEPS = 8;
     static constexpr int JT = 16;
-    static constexpr int TILE = 32, NG = 2, B_TOK = 16, B_BYTES = 0;
+    static constexpr int TILE = 32, NG = 2, B_TOK = 16, B_BYTES = 0, ROW = 256;
     typedef half8 PopT;
     template <int RT>
     __device__ static void qk(const TileK& t, float4v (&sacc)[2][RT], const half8 (&qop)[RT][KSTEPS]) {
@@ -193,7 +194,7 @@ template <> struct Fmt<kFmtF16D128> {
     static constexpr int D = 128;
     static constexpr int KSTEPS = 4;
     static constexpr int JT = 8;
-    static constexpr int TILE = 32, NG = 2, B_TOK = 16, B_BYTES = 0;
+    static constexpr int TILE = 32, NG = 2, B_TOK = 16, B_BYTES = 0, ROW = 256;
     typedef half8 PopT;
     template <int RT>
     __device__ static void qk(const TileK& t, float4v (&sacc)[2][RT], const half8 (&qop)[RT][KSTEPS]) {
@@ -234,7 +235,7 @@ template <> struct Fmt<kFmtF16D256> {
     static constexpr int D = 256;
     static constexpr int KSTEPS = 8;
     static constexpr int JT = 16;
-    static constexpr int TILE = 16, NG = 1, B_TOK = 0, B_BYTES = 256;
+    static constexpr int TILE = 16, NG = 1, B_TOK = 0, B_BYTES = 256, ROW = 256;
     typedef half4 PopT;
     __device__ static int q_dim(int ks, int qd) { return 32 * ks + 8 * qd; }
     __device__ static int o_dim(int qd, int i, int j) { return j < 8 ? 8 * (4 * qd + i) + j : 128 + 8 * (4 * qd + i) + j - 8; }
@@ -272,6 +273,76 @@ template <> struct Fmt<kFmtF16D256> {
     }
 };
 
+// E4M3, D = 128: 128-byte token rows, 32-token tiles of two 16-token granules. K vector i
+// (i = 0, 1) of a lane holds dims 64*i + 16*qd + 0..15 and feeds k-steps 2i and 2i+1, as at
+// D = 256. For PV, lane (m, qd) needs dims 8m..8m+7 of its 8 tokens: each V slot holds the 16-byte
+// pair of dims 16*(m/2) + 0..15 (lanes m and m^1 load the same bytes, from the same cache
+// line), and the lane keeps its own half. MFMA j (0..7) covers dims 8m + j.
+template <> struct Fmt<kFmtE4M3D128> {
+    static constexpr int D = 128;
+    static constexpr int KSTEPS = 4;
+    static constexpr int JT = 8;
+    static constexpr int TILE = 32, NG = 2, B_TOK = 16, B_BYTES = 0, ROW = 128;
+    typedef half8 PopT;
+    __device__ static int q_dim(int ks, int qd) { return 64 * (ks >> 1) + 16 * qd + 8 * (ks & 1); }
+    __device__ static half8 k_op(const u32x4 (&k)[4], int ks) {
+        const u32x4 w = k[ks >> 1];
+        return (ks & 1) ? e4m3x8(w[2], w[3]) : e4m3x8(w[0], w[1]);
+    }
+    __device__ static int o_dim(int qd, int i, int j) { return 8 * (4 * qd + i) + j; }
+    template <int RT>
+    __device__ static void qk(const TileK& t, float4v (&sacc)[2][RT], const half8 (&qop)[RT][KSTEPS]) {
+        qk_two_granules<Fmt<kFmtE4M3D128>, RT>(t, sacc, qop);
+    }
+    template <int RT>
+    __device__ static void pv(const TileV& t, const half8 (&pop)[RT], float4v (&o)[RT][JT]) {
+        const bool upper = threadIdx.x & 1;          // lane parity: the upper 8 bytes are this lane's
+        uint32_t dw[8][2];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            dw[e][0] = upper ? t.v[e][2] : t.v[e][0];
+            dw[e][1] = upper ? t.v[e][3] : t.v[e][1];
+        }
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+#pragma unroll
+            for (int cp = 0; cp < 2; ++cp) {
+                half8 a0, a1;
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp) {
+                    half2v lo, hi;
+                    DecE4M3::pair(dw[2 * pp + 1][w], dw[2 * pp][w], cp, lo, hi);
+                    a0[2 * pp] = lo[0];
+                    a0[2 * pp + 1] = lo[1];
+                    a1[2 * pp] = hi[0];
+                    a1[2 * pp + 1] = hi[1];
+                }
+                const int jd = 4 * w + 2 * cp;
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    o[rt][jd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, pop[rt], o[rt][jd], 0, 0, 0);
+                    o[rt][jd + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, pop[rt], o[rt][jd + 1], 0, 0, 0);
+                }
+            }
+        }
+    }
+};
+
+// Row geometry of a format: K loads per granule (1 KB each), rows per load, lanes per row, the
+// chunk-swizzle key of a token, and the byte offset of a lane's V slot within a row.
+template <class F>
+struct Geo {
+    static constexpr int KL = F::ROW / 64;            // 4 (256-byte rows) or 2 (128-byte rows)
+    static constexpr int RPI = 1024 / F::ROW;         // token rows per load instruction
+    static constexpr int LPR = F::ROW / 16;           // lanes per token row
+    static constexpr int CH = F::ROW / 64;            // 16-byte K chunks a lane reads per granule token
+    // K chunk c of token t sits in LDS slot c ^ swz(t): with rows 256 bytes apart the 16 lanes of
+    // an MFMA-order read (16 tokens, one chunk) then hit 16 bank groups; 128-byte rows pair up.
+    __device__ static int swz(int t) { return F::ROW == 256 ? t : (t >> 1); }
+    __device__ static int v_lane_byte(int n) { return F::ROW == 256 ? 16 * n : 16 * (n >> 1); }
+    static constexpr int KLOADS = 2 * KL, VLOADS = 8;   // per tile and wave
+};
+
 // Page and slot of logical token j (a granule start): j / page_size by a multiply-shift with
 // the host-computed reciprocal ceil(2^40 / page_size), exact for j < 2^20 and page_size < 2^20.
 __device__ __forceinline__ void locate(int32_t j, const RunParams& p, int32_t& page_idx, int32_t& slot) {
@@ -293,16 +364,18 @@ struct LaneOffs {
     uint32_t v[4];
 };
 
+template <class F>
 __device__ __forceinline__ LaneOffs lane_offsets(const RunParams& p, int lane, int n, int qd) {
+    using G = Geo<F>;
     LaneOffs o;
-    const int tr = lane >> 4, slot = lane & 15;
+    const int tr = lane / G::LPR, slot = lane % G::LPR;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int tok = 4 * i + tr;                    // token within the granule
-        o.k[i] = (uint32_t)(tok * p.k_token_stride + 16 * (slot ^ tok));
+        const int tok = G::RPI * i + tr;               // token within the granule (i < KL used)
+        o.k[i] = (uint32_t)(tok * p.k_token_stride + 16 * (slot ^ G::swz(tok)));
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o.v[e] = (uint32_t)((4 * qd + e) * p.v_token_stride + 16 * n);
+    for (int e = 0; e < 4; ++e) o.v[e] = (uint32_t)((4 * qd + e) * p.v_token_stride + G::v_lane_byte(n));
     return o;
 }
 
@@ -366,25 +439,25 @@ constexpr int kStageBytes = kStageRows * 64 * 16;
 template <class F>
 __device__ __forceinline__ void issue_k(const Granules& gr, int32_t last, const LaneOffs& lo, uint32_t stage,
                                         const RunParams& p, int lane) {
+    using G = Geo<F>;
     if (gr.j0 + F::TILE - 1 <= last && !gr.past_end) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < G::KL; ++i) {
             dma16(gr.kA, lo.k[i], stage + i * 1024);
-            dma16(gr.kB, lo.k[i], stage + (4 + i) * 1024);
+            dma16(gr.kB, lo.k[i], stage + (G::KL + i) * 1024);
         }
     } else {
-        const int tr = lane >> 4, slot = lane & 15;
+        const int tr = lane / G::LPR, slot = lane % G::LPR;
         const int32_t cap = gr.past_end ? gr.j0 : last;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tok = 4 * i + tr;
-            const uint32_t oa =
-                (uint32_t)((min(gr.j0 + tok, last) - gr.j0) * p.k_token_stride + 16 * (slot ^ tok));
-            const uint32_t ob =
-                (uint32_t)((min(gr.j0 + F::B_TOK + tok, last) - gr.gsB) * p.k_token_stride + 16 * (slot ^ tok));
-            dma16(gr.kA, gr.past_end ? (uint32_t)((last - cap) * p.k_token_stride + 16 * slot) : oa, stage + i * 1024);
-            dma16(gr.kB, gr.past_end ? (uint32_t)((last - cap) * p.k_token_stride + 16 * slot) : ob,
-                  stage + (4 + i) * 1024);
+        for (int i = 0; i < G::KL; ++i) {
+            const int tok = G::RPI * i + tr;
+            const uint32_t sw = 16 * (slot ^ G::swz(tok));
+            const uint32_t oa = (uint32_t)((min(gr.j0 + tok, last) - gr.j0) * p.k_token_stride) + sw;
+            const uint32_t ob = (uint32_t)((min(gr.j0 + F::B_TOK + tok, last) - gr.gsB) * p.k_token_stride) + sw;
+            const uint32_t oz = (uint32_t)((last - cap) * p.k_token_stride + 16 * slot);
+            dma16(gr.kA, gr.past_end ? oz : oa, stage + i * 1024);
+            dma16(gr.kB, gr.past_end ? oz : ob, stage + (G::KL + i) * 1024);
         }
     }
 }
@@ -392,6 +465,7 @@ __device__ __forceinline__ void issue_k(const Granules& gr, int32_t last, const 
 template <class F>
 __device__ __forceinline__ void issue_v(const Granules& gr, int32_t last, const LaneOffs& lo, uint32_t stage,
                                         const RunParams& p, int n, int qd) {
+    const int vb = Geo<F>::v_lane_byte(n);
     if (gr.j0 + F::TILE - 1 <= last && !gr.past_end) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -402,18 +476,24 @@ __device__ __forceinline__ void issue_v(const Granules& gr, int32_t last, const 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int rel = 4 * qd + e;
-            const uint32_t oa = (uint32_t)((min(gr.j0 + rel, last) - gr.j0) * p.v_token_stride + 16 * n);
-            const uint32_t ob = (uint32_t)((min(gr.j0 + F::B_TOK + rel, last) - gr.gsB) * p.v_token_stride + 16 * n);
-            const uint32_t oz = (uint32_t)((last - gr.j0) * p.v_token_stride + 16 * n);
+            const uint32_t oa = (uint32_t)((min(gr.j0 + rel, last) - gr.j0) * p.v_token_stride + vb);
+            const uint32_t ob = (uint32_t)((min(gr.j0 + F::B_TOK + rel, last) - gr.gsB) * p.v_token_stride + vb);
+            const uint32_t oz = (uint32_t)((last - gr.j0) * p.v_token_stride + vb);
             dma16(gr.vA, gr.past_end ? oz : oa, stage + (8 + e) * 1024);
             dma16(gr.vB, gr.past_end ? oz : ob, stage + (12 + e) * 1024);
         }
     }
 }
 
-// Every tile is 8 K loads then (later) 8 V loads, and a wave keeps two tiles in flight: when
-// tile k's K (or V) is needed, the 24 newer loads of the ring may still be outstanding.
-__device__ __forceinline__ void vm_wait_oldest_half_tile() { asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); }
+// Every tile is KLOADS K loads then (later) VLOADS V loads, and a wave keeps two tiles in
+// flight: when tile k's K is needed, its V and the next tile's loads may still be outstanding;
+// when its V is needed, the next tile's loads and the K loads issued after K(k) was read.
+template <int N>
+__device__ __forceinline__ void vm_wait_n() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+template <class F>
+__device__ __forceinline__ void vm_wait_tile_k() { vm_wait_n<2 * Geo<F>::VLOADS + Geo<F>::KLOADS>(); }
+template <class F>
+__device__ __forceinline__ void vm_wait_tile_v() { vm_wait_n<2 * Geo<F>::KLOADS + Geo<F>::VLOADS>(); }
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
@@ -495,7 +575,7 @@ __device__ __forceinline__ void split_row_max(float (&m)[RT], int32_t j_begin, i
         const uint8_t* rowB = gr.kB + (int64_t)(min(j0 + F::B_TOK + n, last) - gr.gsB) * p.k_token_stride + 16 * qd;
         TileK t;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < Geo<F>::CH; ++i) {
             t.k[0][i] = *reinterpret_cast<const u32x4*>(rowA + 64 * i);
             t.k[1][i] = *reinterpret_cast<const u32x4*>(rowB + 64 * i);
         }
@@ -640,12 +720,12 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void split_kernel(RunParam
     uint8_t* ring = lds.rings[wave];
     const uint32_t ring0 = lds_addr(ring);
     const u32x4* ring_lane = reinterpret_cast<const u32x4*>(ring) + lane;
-    const LaneOffs lo = lane_offsets(p, lane, n, qd);
-    // LDS byte offsets of the consumer's K chunks: token n of granule tt at row 16*tt + n,
-    // chunk 4*i + qd in slot chunk ^ n.
+    const LaneOffs lo = lane_offsets<F>(p, lane, n, qd);
+    // LDS byte offsets of the consumer's K chunks: token n of granule tt at row n of the granule's
+    // rows (ROW bytes each), chunk 4*i + qd in slot chunk ^ swz(n).
     uint32_t k_rd[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) k_rd[i] = n * 256 + 16 * ((4 * i + qd) ^ n);
+    for (int i = 0; i < 4; ++i) k_rd[i] = n * F::ROW + 16 * ((4 * i + qd) ^ Geo<F>::swz(n));
     constexpr int32_t kStride = kWavesPerHead * F::TILE;        // tokens between a wave's tiles
     const int32_t first = j_begin + half * F::TILE;              // this wave's first tile
 
@@ -682,14 +762,14 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void split_kernel(RunParam
             const uint32_t stage = ring0 + st * kStageBytes;
             const u32x4* sl = ring_lane + st * (kStageBytes / 16);
             const Granules gn = granules<F>(j0 + 2 * kStride, last, pages, pg0, kbase, vbase, p);
-            vm_wait_oldest_half_tile();         // tile k's K has landed
+            vm_wait_tile_k<F>();                // tile k's K has landed
             TileK tk;
             const uint8_t* stage_bytes = ring + st * kStageBytes;
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    tk.k[tt][i] = *reinterpret_cast<const u32x4*>(stage_bytes + tt * 4096 + k_rd[i]);
+                for (int i = 0; i < Geo<F>::CH; ++i)
+                    tk.k[tt][i] = *reinterpret_cast<const u32x4*>(stage_bytes + tt * Geo<F>::KL * 1024 + k_rd[i]);
             lds_wait_all();
             issue_k<F>(gn, last, lo, stage, p, lane);
             float4v sacc[2][RT];
@@ -697,7 +777,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void split_kernel(RunParam
             typename F::PopT pop[RT];
             over = softmax_tile<RT, F::NG, F::TILE>(sacc, j0, mask_from, lim, c, m_ref, l_run, pop, qd);
             TileV tv;
-            vm_wait_oldest_half_tile();         // tile k's V has landed
+            vm_wait_tile_v<F>();                // tile k's V has landed
 #pragma unroll
             for (int e = 0; e < 8; ++e) tv.v[e] = sl[(8 + e) * 64];
             lds_wait_all();
@@ -881,7 +961,9 @@ attn_status attn_launch_split(const attn_plan_s* plan, const attn::RunParams& p,
     const int row_tiles = p.rows_alloc / 16;
     const int hp = attn::heads_per_workgroup(p.num_kv_heads, p.batch, p.grid_splits, plan->num_cus);
     attn::KernelFn fn;
-    if (plan->desc.kv_dtype == ATTN_KV_FP16)
+    if (plan->desc.kv_dtype == ATTN_KV_E4M3 && plan->desc.head_dim == 128)
+        fn = attn::split_for<attn::kFmtE4M3D128>(row_tiles, hp);
+    else if (plan->desc.kv_dtype == ATTN_KV_FP16)
         fn = plan->desc.head_dim == 256 ? attn::split_for<attn::kFmtF16D256>(row_tiles, hp)
                                         : attn::split_for<attn::kFmtF16D128>(row_tiles, hp);
     else if (plan->desc.kv_dtype == ATTN_KV_E5M2)

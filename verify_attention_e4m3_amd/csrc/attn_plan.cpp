@@ -29,6 +29,7 @@ constexpr Geometry kGeometries[] = {
     {ATTN_KV_FP16, 128, 8, attn::kMaxRows},
     {ATTN_KV_E5M2, 256, 8, attn::kMaxRows},
     {ATTN_KV_FP16, 256, 8, attn::kMaxRows},
+    {ATTN_KV_E4M3, 128, 8, attn::kMaxRows},
 };
 constexpr int kNumGeometries = sizeof(kGeometries) / sizeof(kGeometries[0]);
 

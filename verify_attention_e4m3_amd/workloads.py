@@ -64,6 +64,11 @@ WORKLOADS = {
                  "B4 x 32768, Hq24/Hkv4, FP16 KV at D256, shuffled pages"),
         Workload("verify_b8_ctx128k_gqa6_fp16_d256_4layers", 8, 131072, 8, 24, 4, 256, 1648, "fp16", 1.0, 1.0, 4,
                  13, 131072, "B8 x 131072, Hq24/Hkv4, FP16 KV at D256 (4.3 GB per layer), 4 per-layer caches"),
+        # E4M3 KV at D128 (another head dimension)
+        Workload("verify_b4_ctx32k_gqa6_e4m3_d128", 4, 32768, 8, 24, 4, 128, 1648, "e4m3", 1.0, 1.0, 1, 14, 32768,
+                 "B4 x 32768, Hq24/Hkv4, E4M3 KV at D128, shuffled pages"),
+        Workload("verify_b8_ctx128k_gqa6_e4m3_d128_16layers", 8, 131072, 8, 24, 4, 128, 1648, "e4m3", 1.0, 1.0, 16,
+                 15, 131072, "B8 x 131072, Hq24/Hkv4, E4M3 KV at D128 (1.07 GB per layer), 16 per-layer caches"),
         # four local query heads on one KV head (the pages' TP4 geometry of another model), q8
         Workload("verify_b8_ctx128k_hq4_hkv1_16layers", 8, 131072, 8, 4, 1, 256, 1648, "e4m3", 1.0, 1.0, 16, 8,
                  131072, "B8 x 131072, q8, Hq4/Hkv1 (32 packed rows), 16 per-layer caches, shuffled pages"),
