@@ -430,3 +430,55 @@ def test_graph_replay_with_changed_inputs_matches_eager():
         eager = run_gpu(c)
         assert torch.equal(replayed.view(torch.int16), eager.view(torch.int16)), rep
         compare(replayed, run_oracle(c))
+
+
+# ---- the tests must be able to fail: planted mistakes in the inputs (all reads stay in bounds) ----
+
+def _mismatch(out, ref):
+    try:
+        compare(out, ref)
+    except AssertionError:
+        return True
+    return False
+
+
+def test_mutation_wrong_head_stride_is_caught():
+    # KV head 1 read 8 bytes from head 0's row instead of its own: the comparison must fail.
+    note("mutation: wrong KV head stride")
+    c = _case(batch=2, seq_lens=[700, 300], q_len=8, num_q_heads=12, num_kv_heads=2, head_dim=256, page_size=32,
+              seed=31)
+    ks = A.contiguous_strides(32, 2, 256, "e4m3")
+    good = run_gpu(c)
+    assert not _mismatch(good, run_oracle(c))
+    bad = run_gpu(c, k_strides=(ks[0], ks[1], 8))
+    assert _mismatch(bad, run_oracle(c))
+
+
+def test_mutation_wrong_page_index_is_caught():
+    # Swapping two fully visible pages would only permute the keys (attention does not see the
+    # order); swapping the first page with the partly filled last one changes the key set.
+    note("mutation: first and last block-table entries swapped")
+    c = _case(batch=1, seq_lens=[100], q_len=8, num_q_heads=6, num_kv_heads=1, head_dim=256, page_size=16, seed=32)
+    ref = run_oracle(c)
+    c["block_table"][0, [0, 6]] = c["block_table"][0, [6, 0]].clone()
+    assert _mismatch(run_gpu(c), ref)
+
+
+def test_canary_zones_around_output_and_workspace_stay_intact():
+    note("canary zones around out and workspace")
+    c = _case(batch=3, seq_lens=[3000, 0, 129], q_len=8, num_q_heads=24, num_kv_heads=4, head_dim=256,
+              page_size=1648, seed=33)
+    plan = plan_for(c)
+    guard = 4096 // 2                                    # FP16 elements per 4 KB guard
+    n_out = c["q"].numel()
+    out_buf = torch.full((guard + n_out + guard,), 12345, dtype=torch.int16, device="cuda")
+    out = out_buf[guard:guard + n_out].view(torch.float16).view(c["q"].shape)
+    ws_floats = plan.workspace_bytes(3) // 4
+    ws_buf = torch.full((1024 + ws_floats + 1024,), -7.0, dtype=torch.float32, device="cuda")
+    ws = ws_buf[1024:1024 + ws_floats]
+    plan.run(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"], c["k_scale"], c["v_scale"],
+             out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert (out_buf[:guard] == 12345).all() and (out_buf[guard + n_out:] == 12345).all()
+    assert (ws_buf[:1024] == -7.0).all() and (ws_buf[1024 + ws_floats:] == -7.0).all()
+    compare(out, run_oracle(c))

@@ -76,3 +76,21 @@ def test_b16_mixed_graph_replays():
         plan.combine(args_e)
         torch.cuda.synchronize()
         assert torch.equal(eager.view(torch.int16), out.view(torch.int16))
+
+
+# The pages' GPU coverage matrix (batch sizes, contexts 3297 .. 262144, page sizes 1024 / 1536 /
+# 1648 / 3296), each checked on sampled (slot, KV head) pairs against the oracle.
+MATRIX = [(2, 3297, 1024), (4, 8192, 1536), (8, 32768, 1648), (16, 131072, 3296), (2, 262144, 1024)]
+
+
+@pytest.mark.parametrize("batch,length,page", MATRIX, ids=[f"B{b}-L{l}-p{p}" for b, l, p in MATRIX])
+def test_coverage_matrix_sampled(batch, length, page):
+    note(f"coverage matrix B{batch} L{length} page {page}")
+    lens = [length - (i % 3) * 97 for i in range(batch)]
+    c = wl.make_case(batch=batch, seq_lens=lens, q_len=8, num_q_heads=24, num_kv_heads=4, head_dim=256,
+                     page_size=page, seed=batch * 7 + page, device="cuda", max_seq_len=length)
+    plan = plan_for(c)
+    out = plan.run(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"], c["k_scale"], c["v_scale"])
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (batch - 1, 3)]
+    compare(out, oracle_pairs(c, pairs))
