@@ -66,6 +66,16 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
     return r;
 }
 
+// Max over lanes l, l^16, l^32, l^48 (the four quarter-wave partials of one MFMA column) with
+// the gfx950 lane swaps: v_permlane32_swap pairs lane l with l^32, v_permlane16_swap pairs l with
+// l^16. Both are VALU operations, so the reduction takes no LDS round trip.
+__device__ __forceinline__ float quad_max(float m) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = max3f(__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    return max3f(__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ int32_t clamp_len(int32_t L, int32_t max_len) {
     return L < 0 ? 0 : (L > max_len ? max_len : L);
 }
@@ -296,12 +306,11 @@ template <> struct Fmt<kFmtE4M3D128> {
     }
     template <int RT>
     __device__ static void pv(const TileV& t, const half8 (&pop)[RT], float4v (&o)[RT][JT]) {
-        const bool upper = threadIdx.x & 1;          // lane parity: the upper 8 bytes are this lane's
-        uint32_t dw[8][2];
+        uint32_t dw[8][2];                           // slot e: this lane's 8 dims (8 bytes) of one token
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            dw[e][0] = upper ? t.v[e][2] : t.v[e][0];
-            dw[e][1] = upper ? t.v[e][3] : t.v[e][1];
+            dw[e][0] = t.v[e][0];
+            dw[e][1] = t.v[e][1];
         }
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
@@ -329,7 +338,10 @@ template <> struct Fmt<kFmtE4M3D128> {
 };
 
 // Row geometry of a format: K loads per granule (1 KB each), rows per load, lanes per row, the
-// chunk-swizzle key of a token, and the byte offset of a lane's V slot within a row.
+// chunk-swizzle key of a token, the V layout, and the LDS ring it implies.
+// 256-byte rows: a tile is 16 KB (K in 1 KB rows 0..7 of its stage, V in rows 8..15), and a
+// wave's ring has 2 stages. 128-byte rows: a tile is 8 KB (K rows 0..3, V rows 4..7), and the
+// same 32 KB of ring hold 4 stages, so a wave keeps as many bytes in flight as at 256 bytes.
 template <class F>
 struct Geo {
     static constexpr int KL = F::ROW / 64;            // 4 (256-byte rows) or 2 (128-byte rows)
@@ -339,8 +351,16 @@ struct Geo {
     // K chunk c of token t sits in LDS slot c ^ swz(t): with rows 256 bytes apart the 16 lanes of
     // an MFMA-order read (16 tokens, one chunk) then hit 16 bank groups; 128-byte rows pair up.
     __device__ static int swz(int t) { return F::ROW == 256 ? t : (t >> 1); }
-    __device__ static int v_lane_byte(int n) { return F::ROW == 256 ? 16 * n : 16 * (n >> 1); }
-    static constexpr int KLOADS = 2 * KL, VLOADS = 8;   // per tile and wave
+    static constexpr int KLOADS = 2 * KL;             // per tile and wave
+    static constexpr int VLOADS = 2 * KL;             // V is stored once, like K
+    static constexpr int STAGE = (KLOADS + VLOADS) * 1024;
+    static constexpr int VROW = KLOADS;               // first 1 KB row of V in a stage
+    static constexpr int NS = F::ROW == 256 ? 2 : 4;  // ring stages per wave
+    // 128-byte rows, V: load instruction e of a granule holds its tokens 8e + vtok(r) in 128-byte
+    // row r, so that the tokens 4 apart that a half wave reads together sit in adjacent 128-byte
+    // rows (other LDS banks): r = 2b + a holds token 4a + b.
+    __device__ static int vtok(int r) { return 4 * (r & 1) + (r >> 1); }
+    __device__ static int vrow(int t) { return 2 * (t & 3) + ((t >> 2) & 1); }
 };
 
 // Page and slot of logical token j (a granule start): j / page_size by a multiply-shift with
@@ -374,8 +394,14 @@ __device__ __forceinline__ LaneOffs lane_offsets(const RunParams& p, int lane, i
         const int tok = G::RPI * i + tr;               // token within the granule (i < KL used)
         o.k[i] = (uint32_t)(tok * p.k_token_stride + 16 * (slot ^ G::swz(tok)));
     }
+    if constexpr (F::ROW == 256) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o.v[e] = (uint32_t)((4 * qd + e) * p.v_token_stride + G::v_lane_byte(n));
+        for (int e = 0; e < 4; ++e) o.v[e] = (uint32_t)((4 * qd + e) * p.v_token_stride + 16 * n);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) o.v[e] = (uint32_t)((8 * e + G::vtok(lane >> 3)) * p.v_token_stride + 16 * (lane & 7));
+        o.v[2] = o.v[3] = 0;
+    }
     return o;
 }
 
@@ -428,9 +454,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// A ring stage holds one tile: 16 rows of 64 lanes x 16 bytes (rows 0..7 K, 8..15 V).
-constexpr int kStageRows = 16;
-constexpr int kStageBytes = kStageRows * 64 * 16;
+// A wave's LDS ring: 32 KB, two 16 KB tiles of 256-byte rows or four 8 KB tiles of 128-byte rows.
+constexpr int kRingBytes = 32 * 1024;
 
 // A tile whose 32 tokens all precede `last` uses the split's fixed lane offsets; the tail tile
 // clamps each lane's token to `last` (whose page exists; the extra tokens are masked). A
@@ -464,36 +489,73 @@ __device__ __forceinline__ void issue_k(const Granules& gr, int32_t last, const 
 
 template <class F>
 __device__ __forceinline__ void issue_v(const Granules& gr, int32_t last, const LaneOffs& lo, uint32_t stage,
-                                        const RunParams& p, int n, int qd) {
-    const int vb = Geo<F>::v_lane_byte(n);
+                                        const RunParams& p, int n, int qd, int lane) {
+    using G = Geo<F>;
+    constexpr int VPG = G::VLOADS / 2;                // V loads per granule
+    const uint32_t v0 = stage + G::VROW * 1024;
     if (gr.j0 + F::TILE - 1 <= last && !gr.past_end) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            dma16(gr.vA, lo.v[e], stage + (8 + e) * 1024);
-            dma16(gr.vB, lo.v[e], stage + (12 + e) * 1024);
+        for (int e = 0; e < VPG; ++e) {
+            dma16(gr.vA, lo.v[e], v0 + e * 1024);
+            dma16(gr.vB, lo.v[e], v0 + (VPG + e) * 1024);
         }
     } else {
+        // 256-byte rows: lane (n, qd) loads dims 16n.. of tokens 4qd + e; 128-byte rows: lane l
+        // loads chunk l % 8 of token 8e + vtok(l / 8).
+        const uint32_t vb = F::ROW == 256 ? 16 * n : 16 * (lane & 7);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int rel = 4 * qd + e;
+        for (int e = 0; e < VPG; ++e) {
+            const int rel = F::ROW == 256 ? 4 * qd + e : 8 * e + G::vtok(lane >> 3);
             const uint32_t oa = (uint32_t)((min(gr.j0 + rel, last) - gr.j0) * p.v_token_stride + vb);
             const uint32_t ob = (uint32_t)((min(gr.j0 + F::B_TOK + rel, last) - gr.gsB) * p.v_token_stride + vb);
             const uint32_t oz = (uint32_t)((last - gr.j0) * p.v_token_stride + vb);
-            dma16(gr.vA, gr.past_end ? oz : oa, stage + (8 + e) * 1024);
-            dma16(gr.vB, gr.past_end ? oz : ob, stage + (12 + e) * 1024);
+            dma16(gr.vA, gr.past_end ? oz : oa, v0 + e * 1024);
+            dma16(gr.vB, gr.past_end ? oz : ob, v0 + (VPG + e) * 1024);
         }
     }
 }
 
-// Every tile is KLOADS K loads then (later) VLOADS V loads, and a wave keeps two tiles in
-// flight: when tile k's K is needed, its V and the next tile's loads may still be outstanding;
-// when its V is needed, the next tile's loads and the K loads issued after K(k) was read.
+// The V operand of a tile from its ring stage: slot e of lane (n, qd) is token 4*qd + (e&3) of
+// granule e>>2. 256-byte rows: its 16 bytes of dims 16n.., stored by this very lane. 128-byte
+// rows: the 8 bytes of dims 8n.. (in v[e][0..1]), from where issue_v placed that token's row.
+template <class F>
+__device__ __forceinline__ TileV read_v(const uint8_t* stage, int n, int qd, int lane) {
+    using G = Geo<F>;
+    TileV tv;
+    const uint8_t* v0 = stage + G::VROW * 1024;
+    if constexpr (F::ROW == 256) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tv.v[e] = *reinterpret_cast<const u32x4*>(v0 + e * 1024 + 16 * lane);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int t = 4 * qd + (e & 3);             // token within granule e >> 2
+            const uint8_t* a = v0 + (2 * (e >> 2) + (t >> 3)) * 1024 + 128 * G::vrow(t & 7) + 8 * n;
+            const uint2 w = *reinterpret_cast<const uint2*>(a);
+            tv.v[e] = u32x4{w.x, w.y, 0u, 0u};
+        }
+    }
+    return tv;
+}
+
+// Every tile is KLOADS K loads then (later) VLOADS V loads, and a wave keeps NS tiles in
+// flight: when tile k's K is needed, its V and the next NS - 1 tiles' loads may still be
+// outstanding; when its V is needed, those tiles' loads and the K loads issued after K(k) was read.
 template <int N>
-__device__ __forceinline__ void vm_wait_n() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ __forceinline__ void vm_wait_n() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 template <class F>
-__device__ __forceinline__ void vm_wait_tile_k() { vm_wait_n<2 * Geo<F>::VLOADS + Geo<F>::KLOADS>(); }
+__device__ __forceinline__ void vm_wait_tile_k() {
+    using G = Geo<F>;
+    vm_wait_n<G::VLOADS + (G::NS - 1) * (G::KLOADS + G::VLOADS)>();
+}
 template <class F>
-__device__ __forceinline__ void vm_wait_tile_v() { vm_wait_n<2 * Geo<F>::KLOADS + Geo<F>::VLOADS>(); }
+__device__ __forceinline__ void vm_wait_tile_v() {
+    using G = Geo<F>;
+    vm_wait_n<(G::NS - 1) * (G::KLOADS + G::VLOADS) + G::KLOADS>();
+}
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
@@ -529,10 +591,7 @@ __device__ __forceinline__ bool softmax_tile(const float4v (&sacc)[2][RT], int32
         float m = NG == 2 ? max3f(max3f(x[rt][0], x[rt][1], x[rt][2]), max3f(x[rt][3], x[rt][4 % NV], x[rt][5 % NV]),
                                   max3f(x[rt][6 % NV], x[rt][7 % NV], x[rt][7 % NV]))
                           : max3f(max3f(x[rt][0], x[rt][1], x[rt][2]), x[rt][3], x[rt][3]);
-        const float m16 = __shfl_xor(m, 16);
-        m = max3f(m, m16, m16);
-        const float m32 = __shfl_xor(m, 32);
-        m = max3f(m, m32, m32);
+        m = quad_max(m);
         m *= c;                                      // c > 0: max commutes with the scale
         mx[rt] = m;
         over |= m > m_ref[rt] + kRefSlack && m_ref[rt] != -INFINITY;
@@ -593,8 +652,7 @@ __device__ __forceinline__ void split_row_max(float (&m)[RT], int32_t j_begin, i
                     if (need_mask) v = (j0 + 16 * tt + 4 * qd + i) < lim[rt] ? v : -INFINITY;
                     mx = fmaxf(mx, v);
                 }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = quad_max(mx);
             m[rt] = fmaxf(m[rt], mx * c);
         }
     }
@@ -614,7 +672,7 @@ constexpr int kWavesPerHead = 2;
 
 template <int HP>
 struct SplitLds {
-    __attribute__((aligned(16))) uint8_t rings[kWavesPerHead * HP][2 * kStageBytes];
+    __attribute__((aligned(16))) uint8_t rings[kWavesPerHead * HP][kRingBytes];
     int32_t pages[kMaxSplitPages];
 };
 
@@ -711,15 +769,17 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void split_kernel(RunParam
     }
     __syncthreads();
 
-    // Per-wave two-stage LDS ring: the wave's k-th tile lives in stage k % 2. Its tiles k+1 and
-    // k+2 are in flight while tile k is computed: tile k+2's K (V) loads are issued into stage
-    // k % 2 as soon as tile k's K (V) has been read into registers. Past the split's end the
-    // prefetches re-read one row, so every iteration issues the same 8 + 8 loads and `vmcnt(24)`
-    // before reading tile k's K (and again before its V) means "that half of tile k has landed":
-    // V gets until after the softmax to arrive. After the tile loops the rings hold the hand-over.
+    // Per-wave LDS ring of NS stages: the wave's k-th tile lives in stage k % NS. Its tiles
+    // k+1 .. k+NS are in flight while tile k is computed: tile k+NS's K (V) loads are issued into
+    // stage k % NS as soon as tile k's K (V) has been read into registers. Past the split's end
+    // the prefetches re-read one row, so every iteration issues the same KLOADS + VLOADS loads
+    // and the fixed vmcnt before reading tile k's K (and again before its V) means "that half of
+    // tile k has landed": V gets until after the softmax to arrive. After the tile loops the
+    // rings hold the hand-over.
+    using G = Geo<F>;
+    static_assert(G::NS * G::STAGE <= kRingBytes, "ring stages must fit in the wave's ring");
     uint8_t* ring = lds.rings[wave];
     const uint32_t ring0 = lds_addr(ring);
-    const u32x4* ring_lane = reinterpret_cast<const u32x4*>(ring) + lane;
     const LaneOffs lo = lane_offsets<F>(p, lane, n, qd);
     // LDS byte offsets of the consumer's K chunks: token n of granule tt at row n of the granule's
     // rows (ROW bytes each), chunk 4*i + qd in slot chunk ^ swz(n).
@@ -748,40 +808,35 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void split_kernel(RunParam
             for (int j = 0; j < JT; ++j) o[rt][j] = float4v{0.f, 0.f, 0.f, 0.f};
         }
         if (first > last) return false;          // a short split may leave a second wave no tile
-        {
-            const Granules g0 = granules<F>(first, last, pages, pg0, kbase, vbase, p);
-            issue_k<F>(g0, last, lo, ring0, p, lane);
-            issue_v<F>(g0, last, lo, ring0, p, n, qd);
-            const Granules g1 = granules<F>(first + kStride, last, pages, pg0, kbase, vbase, p);
-            issue_k<F>(g1, last, lo, ring0 + kStageBytes, p, lane);
-            issue_v<F>(g1, last, lo, ring0 + kStageBytes, p, n, qd);
+#pragma unroll
+        for (int k = 0; k < G::NS; ++k) {
+            const Granules gk = granules<F>(first + k * kStride, last, pages, pg0, kbase, vbase, p);
+            issue_k<F>(gk, last, lo, ring0 + k * G::STAGE, p, lane);
+            issue_v<F>(gk, last, lo, ring0 + k * G::STAGE, p, n, qd, lane);
         }
         bool over = false;
         int32_t j0 = first;
-        for (int st = 0;; st ^= 1) {
-            const uint32_t stage = ring0 + st * kStageBytes;
-            const u32x4* sl = ring_lane + st * (kStageBytes / 16);
-            const Granules gn = granules<F>(j0 + 2 * kStride, last, pages, pg0, kbase, vbase, p);
+        for (int st = 0;; st = (st + 1) % G::NS) {
+            const uint32_t stage = ring0 + st * G::STAGE;
+            const uint8_t* stage_bytes = ring + st * G::STAGE;
+            const Granules gn = granules<F>(j0 + G::NS * kStride, last, pages, pg0, kbase, vbase, p);
             vm_wait_tile_k<F>();                // tile k's K has landed
             TileK tk;
-            const uint8_t* stage_bytes = ring + st * kStageBytes;
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int i = 0; i < Geo<F>::CH; ++i)
-                    tk.k[tt][i] = *reinterpret_cast<const u32x4*>(stage_bytes + tt * Geo<F>::KL * 1024 + k_rd[i]);
+                for (int i = 0; i < G::CH; ++i)
+                    tk.k[tt][i] = *reinterpret_cast<const u32x4*>(stage_bytes + tt * G::KL * 1024 + k_rd[i]);
             lds_wait_all();
             issue_k<F>(gn, last, lo, stage, p, lane);
             float4v sacc[2][RT];
             F::template qk<RT>(tk, sacc, qop);
             typename F::PopT pop[RT];
             over = softmax_tile<RT, F::NG, F::TILE>(sacc, j0, mask_from, lim, c, m_ref, l_run, pop, qd);
-            TileV tv;
             vm_wait_tile_v<F>();                // tile k's V has landed
-#pragma unroll
-            for (int e = 0; e < 8; ++e) tv.v[e] = sl[(8 + e) * 64];
+            const TileV tv = read_v<F>(stage_bytes, n, qd, lane);
             lds_wait_all();
-            issue_v<F>(gn, last, lo, stage, p, n, qd);
+            issue_v<F>(gn, last, lo, stage, p, n, qd, lane);
             if (over) break;
             F::template pv<RT>(tv, pop, o);
             j0 += kStride;

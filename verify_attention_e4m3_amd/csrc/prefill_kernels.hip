@@ -57,6 +57,15 @@ constexpr int kPfStageBytes = kPfBlock * kPfRowBytes;        // 16 KB: one K (or
 constexpr int kPfLoadsPerWave = kPfStageBytes / 1024 / kPfWaves;   // 4 K + 4 V per wave and block
 constexpr float kPfSlack = 10.0f;                            // log2 headroom over the reference
 
+// Max over lanes l, l^16, l^32, l^48 (one MFMA column's four quarter-wave partials) with the
+// gfx950 lane swaps (v_permlane32_swap: l <-> l^32, v_permlane16_swap: l <-> l^16), VALU only.
+__device__ __forceinline__ float pf_quad_max(float m) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ uint32_t pf_lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -229,8 +238,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
                         sacc[gr][rt][i] = x;
                         mx = fmaxf(mx, x);
                     }
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                mx = pf_quad_max(mx);
                 const float ms = mx * c;
                 // Branch-free, so that the whole iteration is one scheduling region: the max pass
                 // keeps the running maximum, the others set a row's reference on its first
