@@ -17,15 +17,15 @@
 //    right after the one barrier of an iteration all four waves issue direct global -> LDS loads
 //    three blocks ahead. The loop is software-pipelined: iteration b computes S of block b+1,
 //    whose MFMAs do not depend on (and so overlap) the softmax VALU work of block b, then block
-//    b's softmax and PV. 16-byte chunks of a
-//    token row are XOR-swizzled by token (chunk ^ token % 16), so the MFMA-order LDS reads of 16
-//    lanes hit 16 different bank groups for both K and V.
+//    b's softmax and PV. The 16-byte chunks of a K row are XOR-swizzled by token (chunk ^
+//    token % 16), so the MFMA-order LDS reads of 16 lanes hit 16 different bank groups; V rows
+//    swizzle whole 32-byte chunk pairs (pair ^ token % 16) for the transposed reads below.
 //  * S^T = K . Q^T and O^T += V^T . P^T on v_mfma_f32_16x16x32_f16 with the query rows on the
 //    N dimension: a lane holds one query row in both products, so softmax statistics stay
 //    lane-local apart from a reduction over the 4 lanes of a row, and P feeds the second MFMA
-//    from registers (the PV contraction visits keys in the order S^T holds them). Lane m of the
-//    PV A operand holds dims 8m..8m+7 and 128+8m..128+8m+7 of 8 keys, one 16-byte LDS read per
-//    key and half; a permute pairs keys per dim.
+//    from registers (the PV contraction visits keys in the order S^T holds them). The PV A
+//    operand (16 dims x 8 keys per lane group) comes straight from the row-major V block through
+//    gfx950's transposed LDS read (ds_read_b64_tr_b16), two reads per dim tile.
 //  * Softmax in log2 units against a fixed per-row reference (the maximum of the first block in
 //    which the row sees a key), so the O accumulators are only ever touched by MFMAs. A later
 //    block may exceed the reference by up to 2^10 (exact range in FP16 and FP32); if any row of
@@ -44,6 +44,9 @@ namespace attn {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -89,8 +92,9 @@ struct PrefillLds {
 
 // Loads of one key block: 16 instructions for K and 16 for V, each covering two 512-byte token
 // rows; wave w issues instructions 4w .. 4w+3 of both. Lane l of instruction i writes LDS row
-// 2i + l/32, slot l%32, and fetches that row's chunk (l%32) ^ (row%16). Rows past the sequence
-// re-read its last token (they are masked).
+// 2i + l/32, slot l%32, and fetches that row's 16-byte chunk (l%32) ^ (row%16) for K and
+// (l%32) ^ 2*(row%16) for V (V is read in 32-byte pieces, so its swizzle moves whole pairs of
+// chunks). Rows past the sequence re-read its last token (they are masked).
 __device__ __forceinline__ void pf_issue_block(const PrefillParams& p, const uint8_t* kbase, const uint8_t* vbase,
                                                int32_t blk, uint32_t k_stage, uint32_t v_stage, int wave,
                                                int lane) {
@@ -104,9 +108,10 @@ __device__ __forceinline__ void pf_issue_block(const PrefillParams& p, const uin
         const int i = wave * kPfLoadsPerWave + u;
         const int row = 2 * i + (lane >> 5);
         const int src_row = min(row, last);
-        const uint32_t chunk = (uint32_t)(slot ^ (row & 15)) * 16;
-        pf_dma16(kb, (uint32_t)(src_row * p.k_token_stride * 2) + chunk, k_stage + i * 1024);
-        pf_dma16(vb, (uint32_t)(src_row * p.v_token_stride * 2) + chunk, v_stage + i * 1024);
+        const uint32_t kchunk = (uint32_t)(slot ^ (row & 15)) * 16;
+        const uint32_t vchunk = (uint32_t)(slot ^ (2 * (row & 15))) * 16;
+        pf_dma16(kb, (uint32_t)(src_row * p.k_token_stride * 2) + kchunk, k_stage + i * 1024);
+        pf_dma16(vb, (uint32_t)(src_row * p.v_token_stride * 2) + vchunk, v_stage + i * 1024);
     }
 }
 
@@ -260,32 +265,26 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
                     }
             }
             // O^T += V^T . P^T over the block's keys in the order 4*qd + e (e < 4) of granule 0,
-            // then 16 + 4*qd + e - 4 (e >= 4), as P holds them.
+            // then 16 + 4*qd + e - 4 (e >= 4), as P holds them. The V^T operand of dim tile jd
+            // (dims 16*jd + 0..15) comes from two transposed LDS reads (ds_read_b64_tr_b16): in
+            // each 16-lane group, lane n points at 4 dims (16*jd + 4*(n%4) ..) of key base + n/4,
+            // and lane n receives dim 16*jd + n of the group's 4 keys. Group qd reads keys 4*qd..
+            // (base 0) and 16 + 4*qd.. (base 16, 8 KB further in the stage).
             const uint8_t* vst = stage_v(blk);
+            const int vrow = 4 * qd + (n >> 2);                  // < 16: row % 16 of both reads
+            const uint32_t vlane = (uint32_t)(vrow * kPfRowBytes + 8 * (n & 3));
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                u32x4 tv[8];
+            for (int jd = 0; jd < 16; ++jd) {
+                const uint8_t* a0 = vst + vlane + (uint32_t)(32 * (jd ^ vrow));
+                const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) short4v*)(__attribute__((address_space(3))) const void*)a0);
+                const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) short4v*)(__attribute__((address_space(3))) const void*)(
+                        a0 + 16 * kPfRowBytes));
+                const half8 ah = __builtin_bit_cast(half8, short8v{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int row = 16 * (e >> 2) + 4 * qd + (e & 3);
-                    const int chunk = (16 * hf + n) ^ (row & 15);
-                    tv[e] = *reinterpret_cast<const u32x4*>(vst + row * kPfRowBytes + chunk * 16);
-                }
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const uint32_t sel = h ? 0x07060302u : 0x05040100u;
-                        u32x4 a;
-#pragma unroll
-                        for (int pp = 0; pp < 4; ++pp) a[pp] = __builtin_amdgcn_perm(tv[2 * pp + 1][w], tv[2 * pp][w], sel);
-                        const half8 ah = __builtin_bit_cast(half8, a);
-                        const int jd = 8 * hf + 2 * w + h;
-#pragma unroll
-                        for (int rt = 0; rt < RT; ++rt)
-                            o[rt][jd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, pop[rt], o[rt][jd], 0, 0, 0);
-                    }
-                }
+                for (int rt = 0; rt < RT; ++rt)
+                    o[rt][jd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, pop[rt], o[rt][jd], 0, 0, 0);
             }
         };
 
@@ -331,8 +330,8 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
         }
     }
 
-    // Normalise and store: O^T tile j element i of lane (n, qd) is dim 8*(4*qd + i) + j (j < 8)
-    // or 128 + 8*(4*qd + i) + j - 8 (j >= 8) of the lane's row.
+    // Normalise and store: O^T tile j element i of lane (n, qd) is dim 16*j + 4*qd + i of the
+    // lane's row.
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         float l = l_run[rt];
@@ -342,14 +341,12 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;
         uint16_t* orow = p.out + (int64_t)tok[rt] * p.o_token_stride + (int64_t)head[rt] * p.o_head_stride;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 16; ++j) {
+            half4v v;
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                half8 v;
-#pragma unroll
-                for (int u = 0; u < 8; ++u) v[u] = l > 0.0f ? (_Float16)(o[rt][8 * hf + u][i] * inv) : (_Float16)0.0f;
-                *reinterpret_cast<half8*>(orow + 128 * hf + 8 * (4 * qd + i)) = v;
-            }
+            for (int i = 0; i < 4; ++i) v[i] = l > 0.0f ? (_Float16)(o[rt][j][i] * inv) : (_Float16)0.0f;
+            *reinterpret_cast<half4v*>(orow + 16 * j + 4 * qd) = v;
+        }
     }
 }
 
