@@ -445,7 +445,7 @@ __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32
     const uint64_t b64 = (uint64_t)base;
     const uint64_t sbase = join_words((uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32)),
                                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64));
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
                  "v"(voff), "s"(sbase)
                  : "memory", "m0");
 }

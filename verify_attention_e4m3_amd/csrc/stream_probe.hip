@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void stream_read(const u32x4* __restrict__ src
 constexpr int kStage = 16384;
 
 __device__ __forceinline__ void dma16(const uint8_t* g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
                  "v"(g) : "memory", "m0");
 }
 
