@@ -58,12 +58,11 @@ __device__ __forceinline__ half8 e4m3x8(uint32_t lo, uint32_t hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Max of three floats in one v_max3_f32. fmaxf would first quiet each operand (IEEE mode);
-// the scores here are finite or -inf, so no quieting is needed.
+// Max of three floats. Written with the compiler's own max rather than an inline v_max3_f32: its
+// operands are often MFMA results, and the compiler inserts the wait states between an MFMA
+// write and a VALU read only for instructions it can see.
 __device__ __forceinline__ float max3f(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
+    return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
 
 // Max over lanes l, l^16, l^32, l^48 (the four quarter-wave partials of one MFMA column) with
@@ -339,9 +338,11 @@ template <> struct Fmt<kFmtE4M3D128> {
 
 // Row geometry of a format: K loads per granule (1 KB each), rows per load, lanes per row, the
 // chunk-swizzle key of a token, the V layout, and the LDS ring it implies.
-// 256-byte rows: a tile is 16 KB (K in 1 KB rows 0..7 of its stage, V in rows 8..15), and a
-// wave's ring has 2 stages. 128-byte rows: a tile is 8 KB (K rows 0..3, V rows 4..7), and the
-// same 32 KB of ring hold 4 stages, so a wave keeps as many bytes in flight as at 256 bytes.
+// A wave's ring has 2 stages. 256-byte rows: a tile is 16 KB (K in 1 KB rows 0..7 of its stage,
+// V in rows 8..15), 32 KB of ring. 128-byte rows: a tile is 8 KB (K rows 0..3, V rows 4..7),
+// 16 KB of ring, so a workgroup of two head pairs fits twice in a CU's LDS and the kernel can be
+// held to 256 registers (two waves per SIMD), which keeps the score tiles in VGPRs: in
+// accumulation registers every VALU read of them first takes a copy (8% slower at D128).
 template <class F>
 struct Geo {
     static constexpr int KL = F::ROW / 64;            // 4 (256-byte rows) or 2 (128-byte rows)
@@ -355,7 +356,8 @@ struct Geo {
     static constexpr int VLOADS = 2 * KL;             // V is stored once, like K
     static constexpr int STAGE = (KLOADS + VLOADS) * 1024;
     static constexpr int VROW = KLOADS;               // first 1 KB row of V in a stage
-    static constexpr int NS = F::ROW == 256 ? 2 : 4;  // ring stages per wave
+    static constexpr int NS = 2;                      // ring stages per wave
+    static constexpr int RING = NS * STAGE;           // ring bytes per wave
     // 128-byte rows, V: load instruction e of a granule holds its tokens 8e + vtok(r) in 128-byte
     // row r, so that the tokens 4 apart that a half wave reads together sit in adjacent 128-byte
     // rows (other LDS banks): r = 2b + a holds token 4a + b.
@@ -454,8 +456,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// A wave's LDS ring: 32 KB, two 16 KB tiles of 256-byte rows or four 8 KB tiles of 128-byte rows.
-constexpr int kRingBytes = 32 * 1024;
+// Waves per SIMD the compiler is held to: two for 128-byte rows (their 16 KB rings leave room for
+// two workgroups per CU), else one.
+template <int FMT>
+constexpr int split_waves_per_simd() { return Fmt<FMT>::ROW == 128 ? 2 : 1; }
 
 // A tile whose 32 tokens all precede `last` uses the split's fixed lane offsets; the tail tile
 // clamps each lane's token to `last` (whose page exists; the extra tokens are masked). A
@@ -670,14 +674,14 @@ __device__ __forceinline__ void split_row_max(float (&m)[RT], int32_t j_begin, i
 // tenth over one head per workgroup.
 constexpr int kWavesPerHead = 2;
 
-template <int HP>
+template <int HP, int RING>
 struct SplitLds {
-    __attribute__((aligned(16))) uint8_t rings[kWavesPerHead * HP][kRingBytes];
+    __attribute__((aligned(16))) uint8_t rings[kWavesPerHead * HP][RING];
     int32_t pages[kMaxSplitPages];
 };
 
 template <int FMT, int RT, int HP>
-__global__ __launch_bounds__(64 * kWavesPerHead * HP) void split_kernel(RunParams p) {
+__global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>()) void split_kernel(RunParams p) {
     using F = Fmt<FMT>;
     constexpr int D = F::D;
     constexpr int KS = F::KSTEPS;
@@ -755,7 +759,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void split_kernel(RunParam
     // LDS: the waves' rings, then the split's block-table entries (shared by the workgroup's
     // heads), clamped into the caches and staged once: the tile loop then issues no
     // compiler-visible global load (whose wait would also drain the ring).
-    __shared__ SplitLds<HP> lds;
+    __shared__ SplitLds<HP, Geo<F>::RING> lds;
     int32_t* pages = lds.pages;
     int32_t pg0, pg_last, unused_slot;
     locate(j_begin, p, pg0, unused_slot);
@@ -777,7 +781,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP) void split_kernel(RunParam
     // tile k has landed": V gets until after the softmax to arrive. After the tile loops the
     // rings hold the hand-over.
     using G = Geo<F>;
-    static_assert(G::NS * G::STAGE <= kRingBytes, "ring stages must fit in the wave's ring");
+    static_assert(G::NS * G::STAGE <= sizeof(lds.rings[0]), "ring stages must fit in the wave's ring");
     uint8_t* ring = lds.rings[wave];
     const uint32_t ring0 = lds_addr(ring);
     const LaneOffs lo = lane_offsets<F>(p, lane, n, qd);
