@@ -279,6 +279,24 @@ def test_paired_head_workgroups_equal_single_bitwise():
         assert torch.equal(single[0].view(torch.int16), batched[b].view(torch.int16)), b
 
 
+def test_four_head_workgroups_e4m3_d128_equal_single_bitwise():
+    # E4M3 at D128 groups four KV heads per workgroup when the grid is large enough (B8 at Hkv4
+    # and 64K); one slot alone runs one head per workgroup. Both run each head's split the same way.
+    note("four-head workgroups vs single-slot runs, E4M3 D128 B8 Hkv4 max 65536")
+    lens = [3297, 0, 40000, 8, 131, 65536, 1, 20000]
+    c = _case(batch=8, seq_lens=lens, q_len=8, num_q_heads=24, num_kv_heads=4, head_dim=128, page_size=1648,
+              seed=23, max_seq_len=65536)
+    plan = plan_for(c)
+    gs = plan.info["grid_splits"]
+    assert 8 * 1 * gs >= plan.info["num_cus"] > 4 * gs       # batched groups four heads, single does not
+    batched = run_gpu(c, plan)
+    compare(batched, run_oracle(c))
+    for b in range(8):
+        one = {k: (v[b:b + 1] if k in ("q", "block_table", "seq_lens") else v) for k, v in c.items()}
+        single = run_gpu(one, batch_capacity=1)
+        assert torch.equal(single[0].view(torch.int16), batched[b].view(torch.int16)), b
+
+
 def _repaged(c, page_size, seed):
     """The same logical tokens laid out with another page size and a shuffled page order."""
     ps0 = c["page_size"]

@@ -106,4 +106,6 @@ struct attn_plan_s {
 attn_status attn_launch_split(const attn_plan_s* plan, const attn::RunParams& p, void* stream);
 attn_status attn_launch_combine(const attn_plan_s* plan, const attn::RunParams& p, void* stream);
 attn_status attn_device_cus(int device, int* num_cus);
+// Waves per SIMD the split kernel of a (KV dtype, head dim) runs at: 2 for E4M3 at D128, else 1.
+int attn_split_waves_per_simd(int kv_dtype, int head_dim);
 attn_status attn_stream_device(void* stream, int* device);

@@ -997,17 +997,23 @@ KernelFn split_for_rows(int row_tiles) {
     }
 }
 
-// KV heads per split workgroup: pairs when the head count is even and the paired grid still
-// gives every CU a workgroup (a paired workgroup takes a whole CU's LDS); otherwise one head per
-// workgroup, two of which share a CU. Each head's split runs the same waves, tiles and merge
-// either way, so the choice never changes a bit of the result.
-inline int heads_per_workgroup(int num_kv_heads, int batch, int grid_splits, int num_cus) {
-    if (num_kv_heads % 2 != 0) return 1;
-    return (int64_t)batch * (num_kv_heads / 2) * grid_splits >= num_cus ? 2 : 1;
+// KV heads per split workgroup: the largest group (4 for 128-byte rows, whose 16 KB rings let
+// a workgroup of 8 waves fit a CU; 2 otherwise) that divides the head count while the grid
+// still gives every CU a workgroup; otherwise one head per workgroup. The heads of a group read
+// neighbouring rows of the same tokens, so a CU streams longer runs of each token row (4 heads x
+// 128 bytes at E4M3 D128: 4% faster than pairs). Each head's split runs the same waves, tiles
+// and merge whatever the group, so the choice never changes a bit of the result.
+inline int heads_per_workgroup(int num_kv_heads, int batch, int grid_splits, int num_cus, int max_hp) {
+    for (int hp = max_hp; hp > 1; hp /= 2)
+        if (num_kv_heads % hp == 0 && (int64_t)batch * (num_kv_heads / hp) * grid_splits >= num_cus) return hp;
+    return 1;
 }
 
 template <int FMT>
 KernelFn split_for(int row_tiles, int hp) {
+    if constexpr (Fmt<FMT>::ROW == 128) {
+        if (hp == 4) return split_for_rows<FMT, 4>(row_tiles);
+    }
     return hp == 2 ? split_for_rows<FMT, 2>(row_tiles) : split_for_rows<FMT, 1>(row_tiles);
 }
 
@@ -1018,9 +1024,10 @@ attn_status attn_launch_split(const attn_plan_s* plan, const attn::RunParams& p,
     attn::RunParams args = p;
     void* kargs[] = {&args};
     const int row_tiles = p.rows_alloc / 16;
-    const int hp = attn::heads_per_workgroup(p.num_kv_heads, p.batch, p.grid_splits, plan->num_cus);
+    const bool rows128 = plan->desc.kv_dtype == ATTN_KV_E4M3 && plan->desc.head_dim == 128;
+    const int hp = attn::heads_per_workgroup(p.num_kv_heads, p.batch, p.grid_splits, plan->num_cus, rows128 ? 4 : 2);
     attn::KernelFn fn;
-    if (plan->desc.kv_dtype == ATTN_KV_E4M3 && plan->desc.head_dim == 128)
+    if (rows128)
         fn = attn::split_for<attn::kFmtE4M3D128>(row_tiles, hp);
     else if (plan->desc.kv_dtype == ATTN_KV_FP16)
         fn = plan->desc.head_dim == 256 ? attn::split_for<attn::kFmtF16D256>(row_tiles, hp)
@@ -1034,6 +1041,11 @@ attn_status attn_launch_split(const attn_plan_s* plan, const attn::RunParams& p,
     hipError_t e = hipLaunchKernel((const void*)fn, dim3(grid), dim3(64 * attn::kWavesPerHead * hp), kargs, 0,
                                    (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+int attn_split_waves_per_simd(int kv_dtype, int head_dim) {
+    return kv_dtype == ATTN_KV_E4M3 && head_dim == 128 ? attn::split_waves_per_simd<attn::kFmtE4M3D128>()
+                                                       : attn::split_waves_per_simd<attn::kFmtE4M3D256>();
 }
 
 attn_status attn_launch_combine(const attn_plan_s* plan, const attn::RunParams& p, void* stream) {

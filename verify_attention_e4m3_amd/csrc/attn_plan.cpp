@@ -35,15 +35,17 @@ constexpr int kNumGeometries = sizeof(kGeometries) / sizeof(kGeometries[0]);
 
 bool aligned(int64_t v, int64_t a) { return v > 0 && v % a == 0; }
 
-attn::SplitPolicy policy_for(int num_cus, int num_kv_heads) {
+attn::SplitPolicy policy_for(int num_cus, int num_kv_heads, int waves_per_simd) {
     attn::SplitPolicy p;
-    // Aim one wave at every SIMD (4 per CU, two per split) for a typical batch of 8 long rows:
-    // cap = 2 * CUs / (8 * Hkv) splits per (slot, KV head), i.e. 16 at Hkv 4 and 8 at Hkv 8 on
-    // 256 CUs. The cap depends on the device and the head geometry only - never on the batch -
-    // so a request's partitions, and its output bits, are the same alone or batched. Clamped to
-    // [8, 64]: partitions stay <= 262144 / 8 = 32768 tokens (the kernel stages a split's
-    // block-table entries in LDS) and >= 512 tokens (part_min) keep partial traffic small.
-    const int cap = num_cus * 2 / (8 * num_kv_heads);
+    // Aim waves_per_simd waves at every SIMD (two per split) for a typical batch of 8 long rows:
+    // cap = 2 * waves_per_simd * CUs / (8 * Hkv) splits per (slot, KV head), i.e. 16 at Hkv 4
+    // and 8 at Hkv 8 on 256 CUs with one wave per SIMD (32 and 16 for the E4M3 D128 kernel,
+    // which runs two per SIMD). The cap depends on the device and the head geometry only -
+    // never on the batch - so a request's partitions, and its output bits, are the same alone
+    // or batched. Clamped to [8, 64]: partitions stay <= 262144 / 8 = 32768 tokens (the kernel
+    // stages a split's block-table entries in LDS) and >= 512 tokens (part_min) keep partial
+    // traffic small.
+    const int cap = num_cus * 2 * waves_per_simd / (8 * num_kv_heads);
     p.split_cap = cap < 8 ? 8 : (cap > 64 ? 64 : cap);
     p.part_min = 512;
     p.part_align = 256;
@@ -115,7 +117,7 @@ attn_status attn_plan(const attn_desc* d, int device, attn_plan_t* out, size_t* 
     p->desc = *d;
     p->device = device;
     p->num_cus = num_cus;
-    p->policy = policy_for(num_cus, d->num_kv_heads);
+    p->policy = policy_for(num_cus, d->num_kv_heads, attn_split_waves_per_simd(d->kv_dtype, d->head_dim));
     int32_t gs = 0;
     for (int32_t L = 1; L <= d->max_seq_len; ++L) {
         const int32_t s = attn::num_splits(L, p->policy);
