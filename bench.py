@@ -239,11 +239,16 @@ def main():
     kv_bytes = wl.kv_bytes(lens, w.num_kv_heads, w.head_dim, elem)
     token_heads = sum(lens) * w.num_kv_heads
     # split_kernel<format, row tiles, KV heads per workgroup>: format 0 = E4M3 D256, 1 = FP16 D128,
-    # 2 = E5M2 D256, 3 = FP16 D256, 4 = E4M3 D128; 16 packed rows per tile; heads are paired when Hkv is even and the paired
+    # 2 = E5M2 D256, 3 = FP16 D256, 4 = E4M3 D128; 16 packed rows per tile; a workgroup holds the
+    # largest group of KV heads (up to 4 for E4M3 D128, 2 otherwise) that divides Hkv while the
     # grid still covers every CU (the library's rule).
     fmt = {"e4m3": 0 if w.head_dim == 256 else 4, "fp16": 1 if w.head_dim == 128 else 3, "e5m2": 2}[w.kv_format]
     gs = plan.info["grid_splits"]
-    hp = 2 if w.num_kv_heads % 2 == 0 and w.batch * (w.num_kv_heads // 2) * gs >= plan.info["num_cus"] else 1
+    hp = 1
+    for cand in ((4, 2) if fmt == 4 else (2,)):
+        if w.num_kv_heads % cand == 0 and w.batch * (w.num_kv_heads // cand) * gs >= plan.info["num_cus"]:
+            hp = cand
+            break
     kernel_name = f"split_kernel<{fmt}, {-(-plan.info['rows'] // 16)}, {hp}>"
 
     def step(i):
