@@ -778,8 +778,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>(
     // stage k % NS as soon as tile k's K (V) has been read into registers. Past the split's end
     // the prefetches re-read one row, so every iteration issues the same KLOADS + VLOADS loads
     // and the fixed vmcnt before reading tile k's K (and again before its V) means "that half of
-    // tile k has landed": V gets until after the softmax to arrive. After the tile loops the
-    // rings hold the hand-over.
+    // tile k has landed". After the tile loops the rings hold the hand-over.
     using G = Geo<F>;
     static_assert(G::NS * G::STAGE <= sizeof(lds.rings[0]), "ring stages must fit in the wave's ring");
     uint8_t* ring = lds.rings[wave];
@@ -820,10 +819,12 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>(
         }
         bool over = false;
         int32_t j0 = first;
+        // Granules of the tile that refills the current stage; the next one is looked up during
+        // the current tile's MFMAs, so its block-table read does not stall the loop head.
+        Granules gn = granules<F>(first + G::NS * kStride, last, pages, pg0, kbase, vbase, p);
         for (int st = 0;; st = (st + 1) % G::NS) {
             const uint32_t stage = ring0 + st * G::STAGE;
             const uint8_t* stage_bytes = ring + st * G::STAGE;
-            const Granules gn = granules<F>(j0 + G::NS * kStride, last, pages, pg0, kbase, vbase, p);
             vm_wait_tile_k<F>();                // tile k's K has landed
             TileK tk;
 #pragma unroll
@@ -835,12 +836,14 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>(
             issue_k<F>(gn, last, lo, stage, p, lane);
             float4v sacc[2][RT];
             F::template qk<RT>(tk, sacc, qop);
-            typename F::PopT pop[RT];
-            over = softmax_tile<RT, F::NG, F::TILE>(sacc, j0, mask_from, lim, c, m_ref, l_run, pop, qd);
+            // V is read while the QK MFMAs run, so its LDS latency overlaps them and the softmax.
             vm_wait_tile_v<F>();                // tile k's V has landed
             const TileV tv = read_v<F>(stage_bytes, n, qd, lane);
             lds_wait_all();
             issue_v<F>(gn, last, lo, stage, p, n, qd, lane);
+            gn = granules<F>(j0 + (G::NS + 1) * kStride, last, pages, pg0, kbase, vbase, p);
+            typename F::PopT pop[RT];
+            over = softmax_tile<RT, F::NG, F::TILE>(sacc, j0, mask_from, lim, c, m_ref, l_run, pop, qd);
             if (over) break;
             F::template pv<RT>(tv, pop, o);
             j0 += kStride;
