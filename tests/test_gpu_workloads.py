@@ -94,3 +94,26 @@ def test_coverage_matrix_sampled(batch, length, page):
     torch.cuda.synchronize()
     pairs = [(0, 0), (batch - 1, 3)]
     compare(out, oracle_pairs(c, pairs))
+
+
+def test_library_batch_capacity_sampled():
+    # The largest batch the library admits (its reported capacity, 256 slots), short mixed
+    # lengths with zero-length slots among them and 16-token pages: sampled pairs against the
+    # oracle, every zero-length slot exactly +0.
+    from verify_attention_e4m3_amd import attention as A
+    B = A.capabilities()["max_batch"]
+    note(f"library batch capacity B{B}, lengths <= 2048, page 16")
+    rng = np.random.default_rng(83)
+    lens = [int(x) for x in rng.integers(0, 2049, size=B)]
+    for i in range(0, B, 37):
+        lens[i] = 0
+    c = wl.make_case(batch=B, seq_lens=lens, q_len=8, num_q_heads=24, num_kv_heads=4, head_dim=256, page_size=16,
+                     seed=84, device="cuda", max_seq_len=2048)
+    plan = plan_for(c)
+    out = plan.run(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"], c["k_scale"], c["v_scale"])
+    torch.cuda.synchronize()
+    zero = [b for b in range(B) if lens[b] == 0]
+    assert zero and (out[zero].view(torch.int16) == 0).all()
+    live = [b for b in range(B) if lens[b] > 0]
+    pairs = [(live[0], 0), (live[len(live) // 2], 2), (live[-1], 3), (B - 1 if lens[B - 1] else live[-2], 1)]
+    compare(out, oracle_pairs(c, pairs))
