@@ -127,7 +127,9 @@ typedef struct attn_plan_s* attn_plan_t;
 
 typedef struct attn_plan_info {
     int32_t num_cus;             /* compute units the split policy was sized for */
-    int32_t split_cap;           /* at most this many splits per (slot, KV head) */
+    int32_t split_cap;           /* splits per (slot, KV head) for rows of up to 131072 tokens */
+    int32_t partition_max;       /* longer rows: partitions of at most this many tokens, more splits
+                                    (never more than 64 splits per row) */
     int32_t partition_min;       /* shortest token partition of a split */
     int32_t partition_align;     /* partitions are multiples of this many tokens */
     int32_t grid_splits;         /* splits per (slot, KV head) in the launch grid (= max over lengths) */

@@ -175,7 +175,11 @@ def test_partitions_cover_each_row_exactly():
         assert P % info["partition_align"] == 0 and P % 32 == 0
         assert P >= info["partition_min"]
         assert (S - 1) * P < L <= S * P
-        assert 1 <= S <= info["split_cap"] and S <= info["grid_splits"]
+        assert 1 <= S <= 64 and S <= info["grid_splits"]
+        if L <= 131072:
+            assert S <= info["split_cap"]
+        else:
+            assert P <= max(info["partition_max"], -(-L // 64))
         assert P <= 32768
 
 
@@ -190,9 +194,10 @@ def test_grid_covers_every_length():
 def test_split_cap_follows_the_head_geometry(hkv, cap):
     p = plan(num_q_heads=hkv * 6, num_kv_heads=hkv, max_seq_len=262144, page_size=3296)
     assert p.info["split_cap"] == cap
+    assert p.info["partition_max"] == 131072 // cap
     for L in LENGTHS:
         S, P = p.splits(L)
-        assert S <= cap and P <= 32768
+        assert S <= (cap if L <= 131072 else 64) and P <= 32768
 
 
 def test_split_policy_ignores_batch_and_page_size():
@@ -209,6 +214,19 @@ def test_long_rows_fill_the_chip():
     S, P = p.splits(131072)
     assert 8 * 4 * S * 2 == 4 * 256
     assert P == 8192
+
+
+def test_longer_rows_keep_the_128k_partition():
+    # rows past 131072 tokens get more splits of the 131072-token row's partition length, so a
+    # 262144-token row in a mixed batch runs no longer per workgroup than a 131072-token row
+    p = plan(max_seq_len=262144, page_size=3296)
+    assert p.splits(131072) == (16, 8192)
+    assert p.splits(131073) == (17, 8192)
+    assert p.splits(262144) == (32, 8192)
+    assert p.info["grid_splits"] == 32
+    # at Hkv 1 the 64-split ceiling governs: 262144 / 64 = 4096 tokens, as before
+    one = plan(num_q_heads=6, num_kv_heads=1, max_seq_len=262144, page_size=3296)
+    assert one.splits(262144) == (64, 4096) and one.info["grid_splits"] == 64
 
 
 def test_workspace_panel_holds_the_row_tiles():

@@ -27,7 +27,8 @@ int main() {
 
 
 def test_split_policy_host_copy_matches_partitions(tmp_path):
-    # partition_len / num_splits compiled for the host cover [0, L) with <= cap partitions
+    # partition_len / num_splits compiled for the host cover [0, L): cap partitions up to
+    # 131072 tokens, partitions of at most part_max (or L / 64) past it, never over 64 splits
     src = tmp_path / "pol.cpp"
     src.write_text(r'''
 #include <cstdio>
@@ -36,9 +37,13 @@ int main() {
     const int caps[] = {8, 16, 32, 64};
     for (int cap : caps)
         for (int L = 1; L <= 262144; L += 37) {
-            attn::SplitPolicy p{cap, 512, 256};
+            attn::SplitPolicy p{cap, attn::kLongLen / cap, 512, 256};
             const int P = attn::partition_len(L, p), S = attn::num_splits(L, p);
-            if (P % 256 || P < 512 || S > cap || (long)(S - 1) * P >= L || (long)S * P < L) return 1;
+            if (P % 256 || P < 512 || S > attn::kMaxSplits || (long)(S - 1) * P >= L || (long)S * P < L) return 1;
+            if (L <= attn::kLongLen && S > cap) return 2;
+            const int fewest = ((L + 63) / 64 + 255) / 256 * 256;
+            if (L > attn::kLongLen && P > (p.part_max > fewest ? p.part_max : fewest)) return 3;
+            if (P > 16384) return 4;
         }
     return 0;
 }

@@ -55,7 +55,8 @@ class attn_desc(ctypes.Structure):
 
 
 class attn_plan_info(ctypes.Structure):
-    _fields_ = [("num_cus", ctypes.c_int32), ("split_cap", ctypes.c_int32), ("partition_min", ctypes.c_int32),
+    _fields_ = [("num_cus", ctypes.c_int32), ("split_cap", ctypes.c_int32), ("partition_max", ctypes.c_int32),
+                ("partition_min", ctypes.c_int32),
                 ("partition_align", ctypes.c_int32), ("grid_splits", ctypes.c_int32), ("rows", ctypes.c_int32),
                 ("split_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t)]
 

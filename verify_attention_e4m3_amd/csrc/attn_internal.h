@@ -30,14 +30,25 @@ constexpr int kWorkspaceAlign = 256;
 // so a request's partial sums - and therefore its output bits - are the same whether it runs
 // alone or batched (the bitwise batched == single requirement of the DFlash2 long-batch note,
 // "Operator validation"). P is a multiple of the kernel tile so tiles never straddle splits.
+// Rows up to kLongLen tokens get split_cap splits; longer rows keep the partition length of a
+// kLongLen row (part_max) and get more splits instead, up to kMaxSplits, so that in a batch of
+// mixed lengths the longest rows do not leave a few long workgroups running alone at the end.
+constexpr int kMaxSplits = 64;         // the combine kernel holds one split per lane
+constexpr int kLongLen = 131072;
+
 struct SplitPolicy {
-    int32_t split_cap;     // at most this many splits per (slot, KV head)
+    int32_t split_cap;     // splits per (slot, KV head) for rows of up to kLongLen tokens
+    int32_t part_max;      // longer rows: partitions of at most this many tokens (but <= kMaxSplits splits)
     int32_t part_min;      // shortest partition
     int32_t part_align;    // partitions are multiples of this (a multiple of kTileTokens)
 };
 
 ATTN_HD int32_t partition_len(int32_t L, SplitPolicy p) {
     int32_t want = (L + p.split_cap - 1) / p.split_cap;
+    if (want > p.part_max) {
+        const int32_t fewest = (L + kMaxSplits - 1) / kMaxSplits;
+        want = p.part_max > fewest ? p.part_max : fewest;
+    }
     want = ((want + p.part_align - 1) / p.part_align) * p.part_align;
     return want < p.part_min ? p.part_min : want;
 }

@@ -42,11 +42,15 @@ attn::SplitPolicy policy_for(int num_cus, int num_kv_heads, int waves_per_simd) 
     // and 8 at Hkv 8 on 256 CUs with one wave per SIMD (32 and 16 for the E4M3 D128 kernel,
     // which runs two per SIMD). The cap depends on the device and the head geometry only -
     // never on the batch - so a request's partitions, and its output bits, are the same alone
-    // or batched. Clamped to [8, 64]: partitions stay <= 262144 / 8 = 32768 tokens (the kernel
+    // or batched. Clamped to [8, 64]: partitions stay <= 131072 / 8 = 16384 tokens (the kernel
     // stages a split's block-table entries in LDS) and >= 512 tokens (part_min) keep partial
-    // traffic small.
+    // traffic small. Rows longer than 131072 tokens keep that row's partition length (part_max:
+    // 8192 tokens at Hkv 4) and get up to 64 splits: in a batch of mixed lengths up to 262144,
+    // halving the longest rows' partitions shortens the run by 14%, at a cost of 6% for a batch
+    // whose rows are all 262144 tokens long (more, shorter workgroups per CU).
     const int cap = num_cus * 2 * waves_per_simd / (8 * num_kv_heads);
     p.split_cap = cap < 8 ? 8 : (cap > 64 ? 64 : cap);
+    p.part_max = attn::kLongLen / p.split_cap;
     p.part_min = 512;
     p.part_align = 256;
     return p;
@@ -143,6 +147,7 @@ attn_status attn_plan_get_info(attn_plan_t p, attn_plan_info* info) {
     if (!p || !info) return ATTN_E_INVALID;
     info->num_cus = p->num_cus;
     info->split_cap = p->policy.split_cap;
+    info->partition_max = p->policy.part_max;
     info->partition_min = p->policy.part_min;
     info->partition_align = p->policy.part_align;
     info->grid_splits = p->grid_splits;
