@@ -262,6 +262,25 @@ def test_batched_equals_single_bitwise():
         assert torch.equal(single[0].view(torch.int16), batched[b].view(torch.int16)), b
 
 
+@pytest.mark.parametrize("hkv", [4, 1])
+def test_rows_past_131072_tokens_batched_equals_single(hkv):
+    # Rows longer than 131072 tokens keep the 131072-token row's partition and get more splits
+    # (32 of 8192 at 262144 tokens and Hkv 4; the 64-split ceiling at Hkv 1): sampled pairs of
+    # the longest row against the oracle, and each row alone gives the batched bits.
+    lens = [262144, 131073, 200001]
+    note(f"rows past 131072 tokens, Hkv{hkv}, lengths {lens}")
+    c = _case(batch=3, seq_lens=lens, q_len=8, num_q_heads=6 * hkv, num_kv_heads=hkv, head_dim=256,
+              page_size=1648, seed=31 + hkv, max_seq_len=262144)
+    plan = plan_for(c)
+    assert plan.splits(262144)[0] == (32 if hkv == 4 else 64)
+    batched = run_gpu(c, plan)
+    compare(batched, oracle_pairs(c, [(0, hkv - 1), (1, 0)]))
+    for b in range(3):
+        one = {k: (v[b:b + 1] if k in ("q", "block_table", "seq_lens") else v) for k, v in c.items()}
+        single = run_gpu(one, batch_capacity=1)
+        assert torch.equal(single[0].view(torch.int16), batched[b].view(torch.int16)), b
+
+
 def test_paired_head_workgroups_equal_single_bitwise():
     # B8 at Hkv4 and 64K fills the chip with workgroups that hold two KV heads each; one slot
     # alone runs one head per workgroup. Both run each head's split the same way.
