@@ -90,6 +90,20 @@ def stream_read_probe(torch, dev, nbytes: int, lds: bool, reps: int = 10) -> flo
     return best
 
 
+def host_cpu() -> dict:
+    """CPU model and logical CPU count of the host the oracle baseline runs on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count()}
+
+
 def cpu_baseline(w, case, budget_s: float = 15.0):
     """The FP64 oracle on (slot, KV head) pairs of layer 0 until about budget_s of CPU work."""
     import numpy as np
@@ -117,7 +131,7 @@ def cpu_baseline(w, case, budget_s: float = 15.0):
     return {"value": round(bytes_total / t_total / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{len(done)} of {len(pairs_all)} (slot, KV head) pairs of layer 0 "
                       f"({bytes_total / 1e9:.3f} GB of KV), FP64 NumPy, {t_total:.1f} s",
-            "ms_per_layer_extrapolated": round(t_total / len(done) * len(pairs_all) * 1e3, 1)}
+            "ms_per_layer_extrapolated": round(t_total / len(done) * len(pairs_all) * 1e3, 1), **host_cpu()}
 
 
 FP16_MFMA_PEAK_TFLOPS = 2500.0
@@ -148,7 +162,7 @@ def prefill_cpu_baseline(w, c, budget_s: float = 15.0):
             break
     return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} query tokens x {w.num_q_heads} heads, each against its visible keys, FP64 NumPy, "
-                      f"{t_total:.1f} s"}
+                      f"{t_total:.1f} s", **host_cpu()}
 
 
 def bench_prefill(args, torch, A, wl):
