@@ -924,9 +924,10 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>(
 // round trip; the max and the denominator are wave reductions in a fixed tree, each split's
 // weight is broadcast from the lane that owns it, and O is summed in split order - the FP32
 // sums are bitwise reproducible.
-template <int D>
+template <int D, int DS>
 __global__ __launch_bounds__(256) void combine_kernel(RunParams p) {
-    constexpr int VW = D / 64;
+    constexpr int VW = D / (64 * DS);                   // dims per lane; a wave covers D / DS dims
+    static_assert(VW >= 1, "at most one dim block per 64 dims");
     constexpr int kChunk = 16;
     typedef float floatv __attribute__((ext_vector_type(VW)));
     typedef _Float16 halfv __attribute__((ext_vector_type(VW)));
@@ -934,6 +935,8 @@ __global__ __launch_bounds__(256) void combine_kernel(RunParams p) {
     const int wave = threadIdx.x >> 6;
     const int row_blocks = (p.rows + 3) / 4;
     int wg = blockIdx.x;
+    const int db = wg % DS;                             // dim block: dims db*D/DS ..
+    wg /= DS;
     const int rb = wg % row_blocks;
     wg /= row_blocks;
     const int g = wg % p.num_kv_heads;
@@ -948,7 +951,7 @@ __global__ __launch_bounds__(256) void combine_kernel(RunParams p) {
     const float* panel0 = p.ws + (int64_t)(b * p.num_kv_heads + g) * p.grid_splits * p.split_floats;
     const int64_t m_off = (int64_t)p.rows_alloc * D + r;
     const int64_t l_off = m_off + p.rows_alloc;
-    const float* orow = panel0 + r * D + VW * lane;
+    const float* orow = panel0 + r * D + db * (D / DS) + VW * lane;
 
     // Split indices past S read split S-1's panel (written by this run, so finite) and get
     // weight 0 from their lane, so the sums need no per-split branches.
@@ -982,7 +985,7 @@ __global__ __launch_bounds__(256) void combine_kernel(RunParams p) {
         }
     }
     const float scale = den > 0.0f ? (*p.v_scale) / den : 0.0f;
-    uint16_t* out = p.out + (((int64_t)b * p.q_len + t) * p.num_q_heads + h) * D + VW * lane;
+    uint16_t* out = p.out + (((int64_t)b * p.q_len + t) * p.num_q_heads + h) * D + db * (D / DS) + VW * lane;
     halfv res;
 #pragma unroll
     for (int i = 0; i < VW; ++i) res[i] = den > 0.0f ? (_Float16)(acc[i] * scale) : (_Float16)0.0f;
@@ -1054,9 +1057,21 @@ int attn_split_waves_per_simd(int kv_dtype, int head_dim) {
 attn_status attn_launch_combine(const attn_plan_s* plan, const attn::RunParams& p, void* stream) {
     attn::RunParams args = p;
     void* kargs[] = {&args};
-    const void* fn = plan->desc.head_dim == 128 ? (const void*)attn::combine_kernel<128>
-                                                : (const void*)attn::combine_kernel<256>;
-    const unsigned grid = (unsigned)p.batch * p.num_kv_heads * ((p.rows + 3) / 4);
+    // Grids with fewer row workgroups than CUs (few slots, KV heads or rows) also split each
+    // row's dims over 2 or 4 waves (B8 x 131072 at Hkv 1: 7.9 -> 6.9 us; no gain on larger
+    // grids). Every wave of a row computes the same weights and sums each of its dims over the
+    // splits in the same order, so the dim split never changes a bit.
+    const int64_t row_wgs = (int64_t)p.batch * p.num_kv_heads * ((p.rows + 3) / 4);
+    const int max_ds = plan->desc.head_dim / 64;
+    int ds = 1;
+    while (ds < max_ds && row_wgs * ds < plan->num_cus) ds *= 2;
+    const void* fn;
+    if (plan->desc.head_dim == 128)
+        fn = ds == 1 ? (const void*)attn::combine_kernel<128, 1> : (const void*)attn::combine_kernel<128, 2>;
+    else
+        fn = ds == 1 ? (const void*)attn::combine_kernel<256, 1>
+                     : (ds == 2 ? (const void*)attn::combine_kernel<256, 2> : (const void*)attn::combine_kernel<256, 4>);
+    const unsigned grid = (unsigned)(row_wgs * ds);
     hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(256), kargs, 0, (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
