@@ -283,3 +283,26 @@ def test_prefill_rejects_null_and_misaligned_pointers():
     assert lib.attn_prefill(None, 4096, 8192, 12288, 16384, None) == A.ATTN_E_INVALID
     assert lib.attn_prefill(ctypes.byref(d), 0, 8192, 12288, 16384, None) == A.ATTN_E_INVALID
     assert lib.attn_prefill(ctypes.byref(d), 4096 + 8, 8192, 12288, 16384, None) == A.ATTN_E_INVALID
+
+
+# ---- host-side checks of run(): caches must hold every byte the kernels may touch ----
+
+def test_cache_extent_and_buffer_checks():
+    import torch
+    p = plan(page_size=32, num_q_heads=12, num_kv_heads=2, max_seq_len=4096)
+    ks = (32 * 2 * 256, 2 * 256, 256)
+    # last byte of the last head row of the last page, for a contiguous cache: exactly its size
+    assert p.cache_extent_bytes(10, ks) == 10 * 32 * 2 * 256
+    # interleaved rows (K and V of a token-head pair 520 bytes apart): D bytes past the last row start
+    assert p.cache_extent_bytes(3, (32 * 2 * 520, 2 * 520, 520)) == 2 * 32 * 2 * 520 + 31 * 2 * 520 + 520 + 256
+    p.device = torch.device("cpu")       # exercise the checks with host tensors
+    k = torch.zeros(10, 32, 2, 256, dtype=torch.uint8)
+    scale = torch.ones(1, dtype=torch.float32)
+    p._validate_caches(k, k, scale, scale, 10)
+    with pytest.raises(ValueError, match="holds"):
+        p._validate_caches(k[:9], k, scale, scale, 10)
+    with pytest.raises(ValueError, match="float32"):
+        p._validate_caches(k, k, scale.double(), scale, 10)
+    with pytest.raises(ValueError, match="float32"):
+        p._validate_caches(k, k, scale, torch.ones(0, dtype=torch.float32), 10)
+    p._validate_caches(12345, 67890, scale, scale, 10)     # raw addresses: the caller vouches

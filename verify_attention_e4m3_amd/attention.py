@@ -221,8 +221,34 @@ class Plan:
         return attn_args(_ptr(q), _ptr(k_cache), _ptr(v_cache), int(num_pages), _ptr(block_table), _ptr(seq_lens),
                          _ptr(k_scale), _ptr(v_scale), ws_ptr, ws_bytes, _ptr(out), int(batch))
 
+    def cache_extent_bytes(self, num_pages: int, strides) -> int:
+        """Bytes from a cache base that the kernels may touch for `num_pages` pages with byte
+        strides (page, token, head): the last byte of the last head row of the last page."""
+        ps, ts, hs = strides
+        return (num_pages - 1) * ps + (self.page_size - 1) * ts + (self.num_kv_heads - 1) * hs + \
+            self.head_dim * ELEM_BYTES[self.kv_dtype]
+
+    def _validate_caches(self, k_cache, v_cache, k_scale, v_scale, num_pages):
+        strides = {"k_cache": (self.desc.k_page_stride, self.desc.k_token_stride, self.desc.k_head_stride),
+                   "v_cache": (self.desc.v_page_stride, self.desc.v_token_stride, self.desc.v_head_stride)}
+        for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+            if isinstance(t, int):
+                continue                       # a raw device address: the caller vouches for its extent
+            if t.device != self.device:
+                raise ValueError(f"{name} is on {t.device}, the plan on {self.device}")
+            need = self.cache_extent_bytes(num_pages, strides[name])
+            have = t.numel() * t.element_size()
+            if have < need:
+                raise ValueError(f"{name} holds {have} bytes; {num_pages} pages at the plan's strides need {need}")
+        for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if t.dtype != torch.float32 or t.numel() < 1 or t.device != self.device:
+                raise ValueError(f"{name} must be a float32 device tensor on {self.device}")
+
     def _validate(self, q, block_table, seq_lens, out):
         B = q.shape[0]
+        for name, t in (("q", q), ("out", out), ("block_table", block_table), ("seq_lens", seq_lens)):
+            if t.device != self.device:
+                raise ValueError(f"{name} is on {t.device}, the plan on {self.device}")
         want = (B, self.q_len, self.num_q_heads, self.head_dim)
         if q.dtype != torch.float16 or tuple(q.shape) != want or not q.is_contiguous():
             raise ValueError(f"q must be contiguous float16 {want}")
@@ -255,6 +281,9 @@ class Plan:
         if out is None:
             out = torch.empty_like(q)
         self._validate(q, block_table, seq_lens, out)
+        if num_pages is None and isinstance(k_cache, int):
+            raise ValueError("num_pages is required when the caches are raw device addresses")
+        self._validate_caches(k_cache, v_cache, k_scale, v_scale, k_cache.shape[0] if num_pages is None else num_pages)
         if workspace is None:
             workspace = (bank or default_bank()).get(self, q.shape[0], stream)
         args = self.make_args(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, out, workspace,
