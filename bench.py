@@ -90,6 +90,17 @@ def stream_read_probe(torch, dev, nbytes: int, lds: bool, reps: int = 10) -> flo
     return best
 
 
+def run_context(torch, dev) -> dict:
+    """What the numbers were measured with: the library's SHA-256 and the device's name and CUs."""
+    from verify_attention_e4m3_amd import attention as A
+    h = hashlib.sha256()
+    with open(A.LIB_PATH, "rb") as f:
+        h.update(f.read())
+    props = torch.cuda.get_device_properties(dev)
+    return {"library_sha256": h.hexdigest(), "device": props.name,
+            "arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count}
+
+
 def host_cpu() -> dict:
     """CPU model and logical CPU count of the host the oracle baseline runs on."""
     model = None
@@ -203,6 +214,7 @@ def bench_prefill(args, torch, A, wl):
                      "unit": "TFLOP/s", "frac": round(achieved / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
                      "kernel": "prefill_kernel", "kernel_ms_mean": round(kms, 4)},
     }
+    res["run"] = run_context(torch, c["q"].device)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = prefill_cpu_baseline(w, c)
     print(json.dumps(res))
@@ -387,6 +399,7 @@ def main():
         "split_frac_of_lds_dma_probe": round(achieved / dma_gbs, 4) if dma_gbs else None,
         "split_ms_p10_p50_p90": [round(x, 5) for x in statistics.quantiles(split_ms, n=10)[0::4]],
     }
+    res["run"] = run_context(torch, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, c0)
     print(json.dumps(res))
