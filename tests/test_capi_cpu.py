@@ -42,7 +42,7 @@ int main(void) {
          sizeof(attn_desc), sizeof(attn_args), sizeof(attn_caps), sizeof(attn_plan_info), sizeof(attn_prefill_desc));
   F(attn_desc, k_page_stride); F(attn_desc, v_head_stride); F(attn_desc, sm_scale); F(attn_desc, causal);
   F(attn_args, num_pages); F(attn_args, workspace_bytes); F(attn_args, out); F(attn_args, batch);
-  F(attn_caps, geometries); F(attn_plan_info, split_bytes);
+  F(attn_caps, geometries); F(attn_plan_info, partition_max); F(attn_plan_info, split_bytes);
   F(attn_prefill_desc, q_token_stride); F(attn_prefill_desc, o_head_stride); F(attn_prefill_desc, sm_scale);
   F(attn_prefill_desc, causal);
   return 0;
@@ -61,6 +61,47 @@ int main(void) {
         if "." in key:
             struct, field = key.split(".")
             assert getattr(getattr(A, struct), field).offset == int(val), key
+
+
+def test_plain_c_caller_links_and_plans(tmp_path):
+    # A C99 program linked against libattn.so: capabilities, a host-only plan of the B8 x 131072
+    # contract, its split policy and workspace size, and a rejected contract - no Python involved.
+    src = tmp_path / "caller.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <string.h>
+#include "attn.h"
+int main(void) {
+  attn_caps caps;
+  if (attn_get_capabilities(&caps) != ATTN_OK || caps.abi_version != ATTN_ABI_VERSION) return 1;
+  attn_desc d;
+  memset(&d, 0, sizeof d);
+  d.abi_version = ATTN_ABI_VERSION; d.kv_dtype = ATTN_KV_E4M3; d.q_len = 8; d.num_q_heads = 24;
+  d.num_kv_heads = 4; d.head_dim = 256; d.page_size = 1648; d.max_pages_per_seq = 80;
+  d.max_seq_len = 131072; d.batch_capacity = 8;
+  d.k_token_stride = d.v_token_stride = 4 * 256; d.k_head_stride = d.v_head_stride = 256;
+  d.k_page_stride = d.v_page_stride = 1648LL * 4 * 256; d.causal = 1;
+  attn_plan_t plan = NULL;
+  size_t ws = 0;
+  if (attn_plan(&d, ATTN_DEVICE_HOST_ONLY, &plan, &ws) != ATTN_OK || !plan) return 2;
+  int32_t s = 0, len = 0;
+  if (attn_plan_splits(plan, 131072, &s, &len) != ATTN_OK) return 3;
+  printf("splits %d %d workspace %zu %zu\n", s, len, ws, attn_plan_workspace_bytes(plan, 8));
+  attn_plan_destroy(plan);
+  d.page_size = 1000;                            /* not a multiple of 16 */
+  attn_status bad = attn_plan(&d, ATTN_DEVICE_HOST_ONLY, &plan, &ws);
+  printf("bad %d %s %d\n", (int)bad, attn_status_string(bad), plan == NULL);
+  return 0;
+}
+''')
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(A.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe), "-L", libdir,
+                    "-lattn", f"-Wl,-rpath,{libdir}"], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
+    assert out[:3] == ["splits", "16", "8192"]
+    assert int(out[4]) == int(out[5]) == plan().workspace_bytes(8)
+    assert " ".join(out[6:]) == f"bad {A.ATTN_E_INVALID} {A.status_string(A.ATTN_E_INVALID)} 1"
 
 
 def test_capabilities():
