@@ -130,6 +130,18 @@ def test_parity_distinct_k_and_v_scales():
     compare(run_gpu(c), run_oracle(c))
 
 
+@pytest.mark.parametrize("k_scale,v_scale", [(-0.75, 1.5), (-2.0, -0.5), (0.0, 1.0)])
+def test_parity_negative_and_zero_scales(k_scale, v_scale):
+    # A negative k_scale flips the sign of every score (the kernel moves it into Q); a negative
+    # v_scale flips the output; k_scale 0 makes every visible key equally likely.
+    note(f"parity k_scale {k_scale}, v_scale {v_scale}")
+    c = _case(batch=2, seq_lens=[333, 2048], q_len=8, num_q_heads=12, num_kv_heads=2, head_dim=256, page_size=32,
+              seed=18)
+    c["k_scale"].fill_(k_scale)
+    c["v_scale"].fill_(v_scale)
+    compare(run_gpu(c), run_oracle(c))
+
+
 def test_power_of_two_scales_are_exact():
     # Scaling by powers of two commutes with FP32/FP16 rounding (no overflow at these values):
     # (2Q, k_scale) and (Q, 2 k_scale) give the same bits, and doubling v_scale doubles every
