@@ -84,8 +84,10 @@ def test_b16_mixed_graph_replays():
 
 
 # The pages' GPU coverage matrix (batch sizes, contexts 3297 .. 262144, page sizes 1024 / 1536 /
-# 1648 / 3296), each checked on sampled (slot, KV head) pairs against the oracle.
-MATRIX = [(2, 3297, 1024), (4, 8192, 1536), (8, 32768, 1648), (16, 131072, 3296), (2, 262144, 1024)]
+# 1648 / 3296), each checked on sampled (slot, KV head) pairs against the oracle; plus the smallest page
+# size at the longest row (16384 block-table entries, 513 of them staged per split).
+MATRIX = [(2, 3297, 1024), (4, 8192, 1536), (8, 32768, 1648), (16, 131072, 3296), (2, 262144, 1024),
+          (1, 262144, 16)]
 
 
 @pytest.mark.parametrize("batch,length,page", MATRIX, ids=[f"B{b}-L{l}-p{p}" for b, l, p in MATRIX])
