@@ -113,6 +113,16 @@ def test_parity_four_query_heads_on_one_kv_head(q_len):
     compare(run_gpu(c), run_oracle(c))
 
 
+@pytest.mark.parametrize("group,q_len", [(3, 8), (5, 8), (8, 6), (12, 4), (16, 3), (48, 1)])
+def test_parity_other_head_groups(group, q_len):
+    # Packed rows q_len * G for groups that are not powers of two or exceed the q8 GQA6 shape
+    # (24 to 48 rows; one to three row tiles, the last one partly filled), two KV heads.
+    note(f"parity G{group} q{q_len}, B2 Hkv2")
+    c = _case(batch=2, seq_lens=[1777, q_len + 3], q_len=q_len, num_q_heads=2 * group, num_kv_heads=2,
+              head_dim=256, page_size=48, seed=300 + group)
+    compare(run_gpu(c), run_oracle(c))
+
+
 def test_parity_non_causal_and_custom_scale():
     note("parity non-causal, sm_scale 0.05")
     c = _case(batch=2, seq_lens=[77, 1500], q_len=8, num_q_heads=6, num_kv_heads=1, head_dim=256, page_size=16,
