@@ -17,7 +17,7 @@ The operation (stated in the pages' terms):
   names the log-sum-exp combine of split partials; ``merge_partials`` is that
   merge written from its definition.
 
-Readings taken where the pages are silent (each one is listed in the design doc):
+Readings taken where the pages are silent:
 
 * the verify tokens are the last ``q_len`` positions of the sequence, so query
   token ``t`` sits at position ``L - q_len + t`` and sees keys ``j <= L - q_len + t``
