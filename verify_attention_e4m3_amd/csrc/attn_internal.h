@@ -34,6 +34,7 @@ constexpr int kWorkspaceAlign = 256;
 // kLongLen row (part_max) and get more splits instead, up to kMaxSplits, so that in a batch of
 // mixed lengths the longest rows do not leave a few long workgroups running alone at the end.
 constexpr int kMaxSplits = 64;         // the combine kernel holds one split per lane
+constexpr int kOrderMaxBatch = 64;     // batches the split kernel orders by work (one slot per lane)
 constexpr int kLongLen = 131072;
 
 struct SplitPolicy {
@@ -93,6 +94,7 @@ struct RunParams {
     int32_t causal;
     int32_t split_floats;         // floats per split panel
     int32_t batch;
+    int32_t order_by_work;        // 1: split workgroups take slots longest partition first
     float sm_scale;
     SplitPolicy policy;
 };

@@ -702,9 +702,26 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>(
     const int g = (wg % head_groups) * HP + hl;
     wg /= head_groups;
     const int s = wg % p.grid_splits;
-    const int b = wg / p.grid_splits;
-
-    const int32_t L = clamp_len(p.seq_lens[b], p.max_seq_len);
+    int b = wg / p.grid_splits;
+    int32_t L;
+    if (p.order_by_work) {
+        // Slot positions in the grid go to the slots in order of decreasing partition length
+        // (then slot index), so the longest-running workgroups are dispatched first and the short
+        // ones fill in behind them. Which workgroup serves a (slot, split) changes nothing in
+        // its arithmetic.
+        const int32_t Ll = lane < p.batch ? clamp_len(p.seq_lens[lane], p.max_seq_len) : 0;
+        const int32_t wk = lane < p.batch ? (Ll > 0 ? partition_len(Ll, p.policy) : 0) : -1;
+        int rank = 0;
+        for (int k = 0; k < p.batch; ++k) {
+            const int32_t wkk = __builtin_amdgcn_readlane(wk, k);
+            rank += (wkk > wk) | ((wkk == wk) & (k < lane));
+        }
+        const uint64_t hit = __ballot(lane < p.batch && rank == b);   // exactly one lane: ranks are a permutation
+        if (hit != 0) b = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+        L = __builtin_amdgcn_readlane(Ll, b);
+    } else {
+        L = clamp_len(p.seq_lens[b], p.max_seq_len);
+    }
     const int32_t S = num_splits(L, p.policy);
     if (s >= S) return;                 // uniform over the workgroup
     const int32_t P = partition_len(L, p.policy);

@@ -234,6 +234,7 @@ attn_status attn_prepare(attn_plan_t p, const attn_args* a, void* stream, attn::
     rp->causal = d.causal;
     rp->split_floats = (int32_t)p->split_floats;
     rp->batch = a->batch;
+    rp->order_by_work = a->batch >= 2 && a->batch <= attn::kOrderMaxBatch;
     rp->sm_scale = p->sm_scale;
     rp->policy = p->policy;
     return ATTN_OK;
