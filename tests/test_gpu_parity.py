@@ -303,6 +303,23 @@ def test_rows_past_131072_tokens_batched_equals_single(hkv):
         assert torch.equal(single[0].view(torch.int16), batched[b].view(torch.int16)), b
 
 
+def test_slot_permutation_permutes_the_output_bitwise():
+    # Workgroups take slots in order of decreasing partition length, so a permuted batch is
+    # served by different workgroups in a different order; every request's bits must follow it.
+    note("slot permutation, B6 mixed lengths")
+    lens = [100, 40000, 3297, 0, 70000, 8]
+    c = _case(batch=6, seq_lens=lens, q_len=8, num_q_heads=24, num_kv_heads=4, head_dim=256, page_size=1648,
+              seed=41, max_seq_len=70000)
+    base = run_gpu(c)
+    perm = [4, 2, 5, 0, 3, 1]
+    pc = dict(c)
+    for k in ("q", "block_table", "seq_lens"):
+        pc[k] = c[k][perm].contiguous()
+    out = run_gpu(pc)
+    assert torch.equal(out.view(torch.int16), base[perm].view(torch.int16))
+    compare(base, oracle_pairs(c, [(4, 0), (1, 3), (2, 1)]))
+
+
 def test_paired_head_workgroups_equal_single_bitwise():
     # B8 at Hkv4 and 64K fills the chip with workgroups that hold two KV heads each; one slot
     # alone runs one head per workgroup. Both run each head's split the same way.
