@@ -24,11 +24,12 @@
  *    that only grow. Section "Operator validation": batched results are bitwise equal to
  *    independent single-request execution; graph replay may change Q and lengths.
  *  - "SM70 attention and quantized projection coverage across TP sizes", section "Scope":
- *    admission by dtype, head grouping, dimensions and alignment, FP16 inputs with FP32
- *    accumulation for QK and PV; section "Compiled-library precision admission": the library
- *    reports its accumulation width (32); section "Additional findings": any positive page size
- *    that is a multiple of 16 is admitted; section "Graph replay and long-prefill follow-up":
- *    captured launches take values as kernel arguments, never host stack addresses.
+ *    admission by dtype, head grouping, dimensions and alignment; FP16 operands, and both
+ *    the score and the value products accumulate in FP32; section "Compiled-library
+ *    precision admission": the library reports its accumulation width (32); section
+ *    "Additional findings": any positive page size that is a multiple of 16 is admitted;
+ *    section "Graph replay and long-prefill follow-up": captured launches take values as
+ *    kernel arguments, never host stack addresses.
  *  - "perf(fa2): port decode GQA group-swap into d128 varlen launcher" (PR #48), description:
  *    the query heads of one KV group are packed into one block so KV is read once per group;
  *    split partials are merged by a log-sum-exp combine.
@@ -156,10 +157,16 @@ typedef struct attn_args {
     int32_t batch;               /* slots in this call, 1 <= batch <= batch_capacity */
 } attn_args;
 
-/* Library capabilities. Errors: ATTN_E_INVALID if caps is NULL. */
+/* Library capabilities: batch capacity, accumulation width, page alignment and the supported
+ * geometries ("DFlash2 ...", section "Why the single-request optimization was missing from
+ * concurrent decode": the library reports its batch capacity; "SM70 ...", section
+ * "Compiled-library precision admission": it reports 32-bit accumulation).
+ * Errors: ATTN_E_INVALID if caps is NULL. */
 ATTN_API attn_status attn_get_capabilities(attn_caps* caps);
 
-/* Validate a contract and build an immutable host plan for HIP device `device` (or
+/* Admission ("SM70 ...", sections "Scope" and "Additional findings": by dtype, head grouping,
+ * dimensions, alignment and page size, never by a tensor-parallel size) and the split policy.
+ * Validate a contract and build an immutable host plan for HIP device `device` (or
  * ATTN_DEVICE_HOST_ONLY). Writes the plan to *plan and, if workspace_bytes is not NULL, the
  * workspace size for batch_capacity slots. No device memory is allocated or read.
  * Errors: ATTN_E_INVALID (null pointers, ABI mismatch, page_size % 16, Hq % Hkv, misaligned
@@ -181,7 +188,11 @@ ATTN_API size_t attn_plan_workspace_bytes(attn_plan_t plan, int32_t batch);
  * split may be shorter). seq_len is clamped to [0, max_seq_len]. Errors: ATTN_E_INVALID. */
 ATTN_API attn_status attn_plan_splits(attn_plan_t plan, int32_t seq_len, int32_t* num_splits, int32_t* partition_len);
 
-/* Split-KV attention: writes the FP32 partial of every (slot, KV head, split) to the workspace.
+/* Split-KV attention over the paged cache ("DFlash2 ...", section "Why the single-request
+ * optimization was missing from concurrent decode": one launch for a whole verify batch with
+ * per-request lengths and FP32 max/sum panels; "perf(fa2) ... PR #48", description: the query
+ * heads of a KV group share one KV read).
+ * Writes the FP32 partial of every (slot, KV head, split) to the workspace.
  * `stream` is a hipStream_t (NULL = the null stream of the current device) and must belong to
  * the plan's device. Asynchronous and capturable into a hipGraph: kernel arguments are values
  * and device pointers only, lengths/scales/queries/tables are read on the device at run time.
@@ -189,7 +200,8 @@ ATTN_API attn_status attn_plan_splits(attn_plan_t plan, int32_t seq_len, int32_t
  * another device), ATTN_E_WORKSPACE, ATTN_E_HIP (launch failed). */
 ATTN_API attn_status attn_run(attn_plan_t plan, const attn_args* args, void* stream);
 
-/* Log-sum-exp combine of the splits written by attn_run (same args, same stream, after it):
+/* The log-sum-exp merge of split partials ("perf(fa2) ... PR #48", description).
+ * Log-sum-exp combine of the splits written by attn_run (same args, same stream, after it):
  * writes every output row of the `batch` slots, +0 for rows that see no key. Same errors. */
 ATTN_API attn_status attn_combine(attn_plan_t plan, const attn_args* args, void* stream);
 

@@ -12,8 +12,8 @@ What it computes follows these pages:
   the kernel contract is E4M3 KV, FP16 queries, D = 256, six query heads per KV
   head, q8 verify batches, zero-length rows and padded requests stay safe.
 * "SM70 attention and quantized projection coverage across TP sizes", section
-  "Scope": FP16 inputs with FP32 accumulation for both QK and PV on the GPU side;
-  the oracle itself works in FP64.
+  "Scope": on the GPU side the operands are FP16 and both products (scores and
+  the weighted sum of values) accumulate in FP32; the oracle itself works in FP64.
 * "perf(fa2): port decode GQA group-swap into d128 varlen launcher" (PR #48),
   PR description: the query heads of one KV group are packed together and read
   KV once per group (head h belongs to KV head h // G).

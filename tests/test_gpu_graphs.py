@@ -122,3 +122,21 @@ def test_graphs_captured_before_the_bank_grows_still_replay():
     ref = _singles(c, caches, qs, rows)
     for o, r in zip(outs, ref):
         assert _same_bits(o, r)
+
+
+def test_hint_past_the_live_table_width_is_rejected_like_the_eager_route():
+    # The live block table is 2 pages wide (3296 tokens), the graphs' window is 8192 tokens: a
+    # hint of 4000 fits the window but not the table, so the graph route must not take it (the
+    # graph's own wider table would hold -1 past the live width); the eager route rejects it.
+    lens = [3000, 17]
+    c, caches, qs = _setup(lens, seed=65, layers=1)
+    gs = VerifyGraphs(_plan(c["block_table"].shape[1], 2), caches, batch_sizes=(2,), bank=A.WorkspaceBank())
+    note("graph set, hint past the live table width")
+    gs.capture()
+    narrow = c["block_table"][:, :2].contiguous()
+    with pytest.raises(ValueError):
+        gs.run(qs, narrow, c["seq_lens"], [4000, 17])
+    outs, route = gs.run(qs, narrow, c["seq_lens"], [3000, 17])      # within the width: the graph
+    assert route == "graph:2"
+    ref = _singles(c, caches, qs, [0, 1])
+    assert _same_bits(outs[0], ref[0])

@@ -27,11 +27,12 @@ def _run_oracle(c, **kw):
                                    kv_format=c["kv_format"], **kw)
 
 
-def _run_brute(c, causal=True):
+def _run_brute(c, causal=True, sm_scale=None):
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(c["head_dim"])
     return np.array(brute_attention(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"],
                                     float(c["k_scale"][0]), float(c["v_scale"][0]), page_size=c["page_size"],
-                                    sm_scale=1.0 / math.sqrt(c["head_dim"]), kv_format=c["kv_format"],
-                                    causal=causal))
+                                    sm_scale=sm_scale, kv_format=c["kv_format"], causal=causal))
 
 
 BRUTE_CASES = [
@@ -63,6 +64,21 @@ def test_oracle_matches_brute_force_non_causal():
     assert np.allclose(got, want, rtol=1e-12, atol=1e-13)
     # and the causal mask does change the answer here
     assert not np.allclose(_run_oracle(c), got)
+
+
+@pytest.mark.parametrize("case_idx", [0, 1, 5])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("sm_scale", [0.05, 0.3])
+def test_oracle_matches_brute_force_explicit_scale(sm_scale, causal, case_idx):
+    # An explicit softmax scale replaces 1/sqrt(D); the brute force applies it to the raw dot
+    # products of its own loops, so a scale that the oracle ignored, applied twice or squared
+    # would show here.
+    c = _case(**BRUTE_CASES[case_idx])
+    got = _run_oracle(c, causal=causal, sm_scale=sm_scale)
+    want = _run_brute(c, causal=causal, sm_scale=sm_scale)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-13), np.abs(got - want).max()
+    # the scale does change the answer at these inputs
+    assert not np.allclose(got, _run_oracle(c, causal=causal), rtol=1e-6, atol=1e-9)
 
 
 def test_row_that_sees_one_key_is_that_value_exactly():
@@ -185,6 +201,50 @@ def test_full_result_is_the_merge_of_split_partials(splits):
         assert np.allclose(merged, want, rtol=1e-13, atol=1e-15)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("sm_scale", [0.05, 0.3])
+def test_partial_states_merge_at_explicit_scale(sm_scale, causal):
+    # partial_states over any token split, merged, equals the full oracle at the same scale and
+    # mask (the full oracle is itself pinned to the brute force at these settings above); the
+    # rows of the last two verify tokens see keys up to the row end, so the causal and the
+    # non-causal partials differ in the final part.
+    c = _case(batch=2, seq_lens=[40, 13], q_len=8, num_q_heads=6, num_kv_heads=2, head_dim=16, page_size=16,
+              seed=29, kv_scale=0.5)
+    full = _run_oracle(c, causal=causal, sm_scale=sm_scale)
+    for b, splits in ((0, [0, 9, 33, 40]), (1, [0, 5, 6, 13])):
+        for g in range(2):
+            parts = [oracle.partial_states(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"], 0.5,
+                                           b=b, kv_head=g, begin=a, end=e, page_size=16, sm_scale=sm_scale,
+                                           causal=causal)
+                     for a, e in zip(splits[:-1], splits[1:])]
+            merged = oracle.merge_partials(parts, 0.5)
+            want = full[b, :, 3 * g:3 * g + 3, :].reshape(24, 16)
+            assert np.allclose(merged, want, rtol=1e-13, atol=1e-15), (b, g)
+    # the brute force agrees with the full result directly
+    assert np.allclose(full, _run_brute(c, causal=causal, sm_scale=sm_scale), rtol=1e-12, atol=1e-13)
+
+
+def test_partial_states_non_causal_sees_every_key():
+    # Non-causal: every row of a part sees all of its keys, so a part holding one key gives that
+    # key's score as m, l = 1 and o = its V row, for every verify token alike.
+    c = _case(batch=1, seq_lens=[20], q_len=4, num_q_heads=2, num_kv_heads=1, head_dim=8, page_size=16, seed=30)
+    m, l, o = oracle.partial_states(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"], 1.0,
+                                    b=0, kv_head=0, begin=19, end=20, page_size=16, sm_scale=0.3, causal=False)
+    page = c["block_table"][0][19 // 16]
+    k19 = oracle.decode_table()[c["k_cache"][page, 19 % 16, 0, :]]
+    v19 = oracle.decode_table()[c["v_cache"][page, 19 % 16, 0, :]]
+    for t in range(4):
+        for j in range(2):
+            r = t * 2 + j
+            s = 0.3 * sum(float(c["q"][0, t, j, d]) * float(k19[d]) for d in range(8))
+            assert math.isclose(m[r], s, rel_tol=1e-13, abs_tol=1e-15)
+            assert l[r] == 1.0 and np.array_equal(o[r], v19)
+    # causal: key 19 is visible only to the last verify token (position 19)
+    m2, l2, _ = oracle.partial_states(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"], 1.0,
+                                      b=0, kv_head=0, begin=19, end=20, page_size=16, sm_scale=0.3, causal=True)
+    assert np.isneginf(m2[:6]).all() and (l2[:6] == 0).all() and (l2[6:] == 1.0).all()
+
+
 def test_merge_of_all_empty_parts_is_zero():
     R, D = 4, 8
     parts = [(np.full(R, -np.inf), np.zeros(R), np.zeros((R, D)))] * 3
@@ -237,3 +297,56 @@ def test_mutation_wrong_head_mapping_is_caught():
     bad = _run_oracle(c2)[:, :, np.argsort(perm), :]
     assert not np.allclose(bad, _run_brute(c), rtol=1e-12, atol=1e-13)
     assert np.allclose(good, _run_brute(c), rtol=1e-12, atol=1e-13)
+
+
+def _mutant_scale_mismatch(monkeypatch, wrap):
+    """Plant a softmax-scale mistake into the oracle's entry point and report whether the
+    explicit-scale brute-force pin notices it."""
+    orig = oa.verify_attention
+
+    def bad(*args, sm_scale=None, **kw):
+        return orig(*args, sm_scale=wrap(sm_scale), **kw)
+    monkeypatch.setattr(oa, "verify_attention", bad)
+    c = _case(**BRUTE_CASES[0])
+    got = oa.verify_attention(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"],
+                              float(c["k_scale"][0]), float(c["v_scale"][0]), page_size=c["page_size"],
+                              kv_format=c["kv_format"], sm_scale=0.3, causal=False)
+    return not np.allclose(got, _run_brute(c, causal=False, sm_scale=0.3), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("mistake", ["ignored", "twice", "squared"])
+def test_mutation_explicit_scale_mistakes_are_caught(monkeypatch, mistake):
+    wrap = {"ignored": lambda s: None, "twice": lambda s: 2 * s, "squared": lambda s: s * s}[mistake]
+    assert _mutant_scale_mismatch(monkeypatch, wrap)
+
+
+def test_mutation_partial_states_scale_ignored_is_caught(monkeypatch):
+    orig = oa.partial_states
+
+    def bad(*args, sm_scale=None, **kw):
+        return orig(*args, **kw)                 # drops the explicit scale
+    monkeypatch.setattr(oa, "partial_states", bad)
+    c = _case(batch=1, seq_lens=[40], q_len=8, num_q_heads=6, num_kv_heads=2, head_dim=16, page_size=16,
+              seed=29, kv_scale=0.5)
+    full = _run_oracle(c, causal=False, sm_scale=0.3)
+    parts = [oa.partial_states(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"], 0.5, b=0,
+                               kv_head=0, begin=a, end=e, page_size=16, sm_scale=0.3, causal=False)
+             for a, e in ((0, 17), (17, 40))]
+    merged = oracle.merge_partials(parts, 0.5)
+    assert not np.allclose(merged, full[0, :, 0:3, :].reshape(24, 16), rtol=1e-13, atol=1e-15)
+
+
+def test_mutation_partial_states_mask_ignored_is_caught(monkeypatch):
+    orig = oa.partial_states
+
+    def bad(*args, causal=True, **kw):
+        return orig(*args, causal=True, **kw)    # always causal
+    monkeypatch.setattr(oa, "partial_states", bad)
+    c = _case(batch=1, seq_lens=[40], q_len=8, num_q_heads=6, num_kv_heads=2, head_dim=16, page_size=16,
+              seed=29, kv_scale=0.5)
+    full = _run_oracle(c, causal=False, sm_scale=0.3)
+    parts = [oa.partial_states(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"], 0.5, b=0,
+                               kv_head=0, begin=a, end=e, page_size=16, sm_scale=0.3, causal=False)
+             for a, e in ((0, 17), (17, 40))]
+    merged = oracle.merge_partials(parts, 0.5)
+    assert not np.allclose(merged, full[0, :, 0:3, :].reshape(24, 16), rtol=1e-13, atol=1e-15)

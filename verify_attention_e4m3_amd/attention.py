@@ -257,8 +257,8 @@ class Plan:
         if block_table.dtype != torch.int32 or tuple(block_table.shape) != (B, self.max_pages_per_seq) or \
                 not block_table.is_contiguous():
             raise ValueError(f"block_table must be contiguous int32 ({B}, {self.max_pages_per_seq})")
-        if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,):
-            raise ValueError(f"seq_lens must be int32 ({B},)")
+        if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,) or not seq_lens.is_contiguous():
+            raise ValueError(f"seq_lens must be contiguous int32 ({B},)")
 
     def split(self, args: attn_args, stream=None):
         """attn_run on `stream` (default: torch's current stream of the plan's device)."""

@@ -139,7 +139,10 @@ class VerifyGraphs:
                 or seq_lens.shape[0] != n:
             raise ValueError("qs, block_table, seq_lens and hints must describe the same live batch")
         B = self.select(hints)
-        if B is None:
+        # A hint longer than the live table can address goes to the eager route, which rejects it
+        # as the ordinary path does (the graph's own table is wider, and its columns past the live
+        # width would hold -1).
+        if B is None or max((int(h) for h in hints), default=0) > block_table.shape[1] * self.plan.page_size:
             return self._run_eager(qs, block_table, seq_lens, hints), "eager"
         st, _, _ = self._static[B]
         W = min(block_table.shape[1], self.plan.max_pages_per_seq)
@@ -147,7 +150,9 @@ class VerifyGraphs:
         for i, q in enumerate(qs):
             st["q"][i][:n].copy_(q)
         st["block_table"].fill_(-1)
-        st["block_table"][:n, :W].copy_(block_table[:, :W])    # hints <= bound: later columns are unused
+        # Every hint is at most W * page_size tokens and at most the captured window, so the
+        # kernels never read a column past W (those hold -1).
+        st["block_table"][:n, :W].copy_(block_table[:, :W])
         st["seq_lens"].zero_()                                   # padded slots are zero-length
         st["seq_lens"][:n].copy_(seq_lens)
         self.stream.wait_stream(cur)
