@@ -445,25 +445,62 @@ def test_repeatable_bitwise():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_reference_slack_overflow_recompute():
-    # The first tile's scores are 0; later spikes score 16 (23 log2 units) above that, beyond
-    # the slack of a row's first-tile reference, so each split is recomputed with exact maxima.
-    note("reference overflow -> exact recompute")
+# One encoding of 1.0 per cache format, for the spiked keys below.
+_ONE = {"e4m3": 0x38, "e5m2": 0x3C, "fp16": 1.0}
+# (kv_format, head_dim) of the five kernels, and q_len at six query heads per KV head giving one,
+# two and three row tiles (12, 24 and 48 packed rows).
+_FORMATS = [("e4m3", 256), ("e5m2", 256), ("fp16", 256), ("fp16", 128), ("e4m3", 128)]
+_ROW_TILES = {1: 2, 2: 4, 3: 8}
+
+
+def _spike_keys(c, spikes, value):
+    """K = 0 for every token of every slot, except `value` (all dims, all KV heads) at the logical
+    tokens `spikes[b]` of slot b."""
+    kc = c["k_cache"]
+    kc.zero_()
+    ps = c["page_size"]
+    for b, js in enumerate(spikes):
+        if not js:
+            continue
+        j = torch.tensor(js, dtype=torch.long, device=kc.device)
+        pages = c["block_table"][b].long()[j // ps]
+        kc[pages, j % ps] = value
+
+
+@pytest.mark.parametrize("row_tiles", [1, 2, 3])
+@pytest.mark.parametrize("fmt,head_dim", _FORMATS, ids=[f"{f}-d{d}" for f, d in _FORMATS])
+@pytest.mark.parametrize("batch", [1, 8])
+def test_reference_slack_overflow_recompute(batch, fmt, head_dim, row_tiles):
+    # Q = 1 everywhere; K is 0 except spikes of 1.0 in every dim, which score sqrt(D) (16 or 11.3,
+    # i.e. 23 or 16 log2 units) above the zero keys. The first 64 tokens of every 512-token split
+    # are zero, so each wave's first tile sets a reference of 0 and a later spike exceeds it by
+    # more than the 2^10 slack: every split is recomputed with its exact row maxima. This runs
+    # the recompute in every kernel (format x row tiles); at B8 (lengths under 1024 tokens and a
+    # 65536-token plan) the workgroups hold two KV heads (four for E4M3 at D128).
+    q_len = _ROW_TILES[row_tiles]
+    lens = [900, 700, 1000, 513, 64, 899, 640, 1023][:batch]
+    note(f"reference overflow -> exact recompute, {fmt} D{head_dim}, {row_tiles} row tiles, B{batch}")
+    c = _case(batch=batch, seq_lens=lens, q_len=q_len, num_q_heads=24, num_kv_heads=4, head_dim=head_dim,
+              page_size=16, seed=14 + batch + head_dim + row_tiles, kv_format=fmt,
+              max_seq_len=65536 if batch > 1 else None)
+    c["q"].fill_(1.0)
+    spikes = [[j for j in range(L) if j % 97 == 0 and j % 512 >= 64] for L in lens]
+    _spike_keys(c, spikes, _ONE[fmt])
+    plan = plan_for(c)
+    if batch > 1:
+        gs, cus = plan.info["grid_splits"], plan.info["num_cus"]
+        hp = 4 if (fmt, head_dim) == ("e4m3", 128) else 2
+        assert batch * (4 // hp) * gs >= cus          # the launch groups hp KV heads per workgroup
+    compare(run_gpu(c, plan), run_oracle(c))
+
+
+def test_reference_slack_mild_rise_single_pass():
+    # A rise of 8.7 log2 units (< the slack) after the first tiles takes the single-pass path.
+    note("reference mild rise, single pass")
     c = _case(batch=1, seq_lens=[900], q_len=8, num_q_heads=6, num_kv_heads=1, head_dim=256, page_size=16,
               seed=14)
     c["q"].fill_(1.0)
-    table = c["block_table"][0].long()
-    kc = c["k_cache"]
-    one = 0x38                        # E4M3 1.0
-    for j in range(0, 64):            # first two tiles: keys 0 -> score 0
-        kc[table[j // 16], j % 16, 0, :] = 0
-    for j in range(64, 900):          # later keys: mostly 0, a few spikes of score 16 (23 log2 units)
-        kc[table[j // 16], j % 16, 0, :] = one if j % 97 == 0 else 0
-    out = run_gpu(c)
-    compare(out, run_oracle(c))
-    # a milder rise (< the slack) takes the single-pass path and must also match
-    for j in range(64, 900):
-        kc[table[j // 16], j % 16, 0, :] = 0x2C if j % 97 == 0 else 0     # 0.375 -> score 6 (8.7 log2 units)
+    _spike_keys(c, [[j for j in range(900) if j % 97 == 0 and j >= 64]], 0x2C)      # 0.375 -> score 6
     compare(run_gpu(c), run_oracle(c))
 
 

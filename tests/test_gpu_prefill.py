@@ -100,7 +100,8 @@ def test_prefill_repeatable_bitwise():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("name", ["prefill_q8192_kv262144_hkv1"])
+@pytest.mark.parametrize("name", ["prefill_q8192_kv262144_hkv1", "prefill_q8192_kv262144_hkv2",
+                                  "prefill_q8192_kv262144_hkv4"])
 def test_prefill_full_size_sampled_tokens(name):
     w = wl.PREFILL_WORKLOADS[name]
     note(f"{name}: sampled tokens")

@@ -1,7 +1,8 @@
 """GPU parity at the full sizes of the long-context workloads, in the launch configuration the
-benchmark times: B8 x 131072, E4M3 and E5M2 (sampled (slot, KV head) pairs checked against the oracle) and
-B16 mixed lengths up to 262144 with page 3296, captured once in a graph and replayed with
-fresh queries, lengths and zero rows."""
+benchmark times: every benchmarked B8 x 131072 workload (E4M3, E5M2 and FP16 at D256, E4M3 at
+D128, Hq4/Hkv1; every output row of layer 0 against the oracle) and B16 mixed lengths up to
+262144 with page 3296, captured once in a graph and replayed with fresh queries, lengths and
+zero rows (every live row of every replay against the oracle)."""
 import numpy as np
 import pytest
 import torch
@@ -15,20 +16,19 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("name", ["verify_b8_ctx128k_gqa6_16layers", "verify_b8_ctx128k_gqa6_e5m2_16layers",
                                   "verify_b8_ctx128k_gqa6_fp16_d256_4layers",
                                   "verify_b8_ctx128k_gqa6_e4m3_d128_16layers", "verify_b8_ctx128k_hq4_hkv1_16layers"])
-def test_b8_ctx128k_sampled_pairs(name):
+def test_b8_ctx128k_full_layer(name):
     # Every benchmarked B8 x 131072 workload, in the launch configuration the benchmark times
-    # (its plan, the full batch, paired / grouped KV heads where the grid allows).
+    # (its plan, the full batch, paired / grouped KV heads where the grid allows): every
+    # (slot, KV head) pair of layer 0, i.e. every output row, against the oracle.
     w = wl.WORKLOADS[name]
-    note(f"{w.name} layer 0, sampled pairs")
+    note(f"{w.name} layer 0, every (slot, KV head) pair")
     c = wl.workload_case(w, device="cuda", layer=0)
     plan = plan_for(c)
     out = plan.run(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"], c["k_scale"], c["v_scale"])
     torch.cuda.synchronize()
-    hkv = w.num_kv_heads
-    pairs = sorted({(0, 0), (w.batch - 1, hkv - 1), (3, 1 % hkv)})
+    pairs = [(b, g) for b in range(w.batch) for g in range(w.num_kv_heads)]
     stats = compare(out, oracle_pairs(c, pairs))
-    assert stats["rows"] == len(pairs) * w.q_len * w.group
-    assert torch.isfinite(out.float()).all()
+    assert stats["rows"] == w.batch * w.q_len * w.num_q_heads
 
 
 def test_b16_mixed_graph_replays():
@@ -66,10 +66,9 @@ def test_b16_mixed_graph_replays():
                 first = out.clone()
         assert torch.equal(first.view(torch.int16), out.view(torch.int16))
         live = [b for b in range(B) if lens[b] > 0]
-        longest = max(live, key=lambda b: lens[b])
-        shortest = min(live, key=lambda b: lens[b])
-        pairs = [(longest, 0), (longest, 3), (shortest, 1), (shortest, 2)]
-        compare(out, oracle_pairs(c, pairs))
+        pairs = [(b, g) for b in live for g in range(w.num_kv_heads)]     # every live row
+        stats = compare(out, oracle_pairs(c, pairs))
+        assert stats["rows"] == len(live) * w.q_len * w.num_q_heads
         for b in range(B):
             if lens[b] == 0:
                 assert (out[b].view(torch.int16) == 0).all(), b
