@@ -69,7 +69,8 @@ typedef enum attn_status {
     ATTN_E_INVALID = 1,      /* bad argument: null pointer, size, alignment, range, ABI mismatch */
     ATTN_E_UNSUPPORTED = 2,  /* well-formed but outside the implemented geometries / dtypes */
     ATTN_E_HIP = 3,          /* a HIP runtime call failed (device query or kernel launch) */
-    ATTN_E_WORKSPACE = 4     /* workspace pointer null or smaller than the plan requires */
+    ATTN_E_WORKSPACE = 4,    /* workspace pointer null or smaller than the plan requires */
+    ATTN_E_STATIC_WORKSPACE = 5  /* attn_run_static: the batch needs more than ATTN_STATIC_WORKSPACE_BYTES */
 } attn_status;
 
 typedef enum attn_kv_dtype {
@@ -207,6 +208,27 @@ ATTN_API attn_status attn_combine(attn_plan_t plan, const attn_args* args, void*
 
 /* Static text for a status code (never NULL). */
 ATTN_API const char* attn_status_string(attn_status status);
+
+/*
+ * Allocation-free attention, for callers that cannot allocate device memory or pass a workspace:
+ * code under hipGraph stream capture, tight serving loops, harnesses that forbid allocation.
+ * Same result as attn_run followed by attn_combine with the same plan and args (the same
+ * kernels, so the same bits), but the split workspace is a static device array inside the
+ * library instead of args->workspace (args->workspace and args->workspace_bytes are ignored).
+ *
+ * The array holds ATTN_STATIC_WORKSPACE_BYTES (64 MiB) on every GPU the library runs on, until
+ * the process ends; its device address is looked up once per device, on the first call there.
+ * A call needs attn_plan_workspace_bytes(plan, args->batch) bytes of it (25.4 MB for 8 rows of
+ * 131072 tokens at Hkv 4, D 256, 48 packed rows); larger batches are refused with
+ * ATTN_E_STATIC_WORKSPACE before anything is launched. Nothing in the array needs to start at
+ * any value: every panel the combine reads is written by the same call's split launch.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on one GPU (two streams,
+ * two threads) race on it and must be serialised by the caller.
+ * Errors: as attn_run, plus ATTN_E_STATIC_WORKSPACE; ATTN_E_HIP if the array's address cannot be
+ * obtained. No HIP allocation, free or synchronisation is made.
+ */
+#define ATTN_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+ATTN_API attn_status attn_run_static(attn_plan_t plan, const attn_args* args, void* stream);
 
 /*
  * Long prefill. Causal attention of a chunk of q_len query tokens against a kv_len-token

@@ -20,7 +20,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     lib = A.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -119,8 +119,9 @@ def test_capabilities():
 
 
 def test_status_strings():
-    for s in range(5):
+    for s in range(6):
         assert A.status_string(s)
+    assert "static" in A.status_string(A.ATTN_E_STATIC_WORKSPACE)
     assert A.status_string(99) == "unknown status"
 
 
@@ -347,3 +348,26 @@ def test_cache_extent_and_buffer_checks():
     with pytest.raises(ValueError, match="float32"):
         p._validate_caches(k, k, scale, torch.ones(0, dtype=torch.float32), 10)
     p._validate_caches(12345, 67890, scale, scale, 10)     # raw addresses: the caller vouches
+
+
+def test_run_static_refuses_host_only_plans_and_null_args():
+    # Host checks only: a host-only plan or a missing argument block is refused before the
+    # library looks up its static array or launches anything.
+    p = A.Plan(q_len=8, num_q_heads=24, num_kv_heads=4, head_dim=256, page_size=1648, max_seq_len=131072,
+               batch_capacity=8)
+    args = A.attn_args()
+    args.batch = 1
+    assert A.lib().attn_run_static(p.handle, ctypes.byref(args), None) == A.ATTN_E_INVALID
+    assert A.lib().attn_run_static(p.handle, None, None) == A.ATTN_E_INVALID
+    assert A.lib().attn_run_static(None, ctypes.byref(args), None) == A.ATTN_E_INVALID
+
+
+def test_static_workspace_covers_the_b8_ctx128k_contract():
+    # The static array (64 MiB) holds the split panels of 8 rows of 131072 tokens at Hkv 4, D 256,
+    # 48 packed rows; 16 rows of up to 262144 tokens need more and are refused on the GPU.
+    p = A.Plan(q_len=8, num_q_heads=24, num_kv_heads=4, head_dim=256, page_size=1648, max_seq_len=131072,
+               batch_capacity=8)
+    assert p.workspace_bytes(8) <= A.ATTN_STATIC_WORKSPACE_BYTES
+    big = A.Plan(q_len=8, num_q_heads=24, num_kv_heads=4, head_dim=256, page_size=3296, max_seq_len=262144,
+                 batch_capacity=16)
+    assert big.workspace_bytes(16) > A.ATTN_STATIC_WORKSPACE_BYTES

@@ -22,7 +22,8 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
 ATTN_ABI_VERSION = 1
-ATTN_OK, ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_HIP, ATTN_E_WORKSPACE = range(5)
+ATTN_OK, ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_HIP, ATTN_E_WORKSPACE, ATTN_E_STATIC_WORKSPACE = range(6)
+ATTN_STATIC_WORKSPACE_BYTES = 64 << 20
 ATTN_KV_E4M3, ATTN_KV_FP16, ATTN_KV_E5M2 = 1, 2, 3
 ATTN_DEVICE_HOST_ONLY = -1
 ATTN_MAX_GEOMETRIES = 8
@@ -92,6 +93,7 @@ EXPORTS = {
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_prefill": (ctypes.c_int, [ctypes.POINTER(attn_prefill_desc), ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "attn_run_static": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(attn_args), ctypes.c_void_p]),
 }
 
 _lib = None
@@ -267,6 +269,23 @@ class Plan:
     def combine(self, args: attn_args, stream=None):
         """attn_combine on `stream` (default: torch's current stream of the plan's device)."""
         _check("attn_combine", lib().attn_combine(self._handle, ctypes.byref(args), self._stream(stream)))
+
+    def run_static(self, q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, *, out=None,
+                   num_pages: Optional[int] = None, stream=None):
+        """attn_run_static: the whole attention with the library's static split workspace (no
+        workspace tensor; calls that overlap on one GPU race on that array). Returns ``out``."""
+        if self.device is None:
+            raise RuntimeError("host-only plan cannot run")
+        if out is None:
+            out = torch.empty_like(q)
+        self._validate(q, block_table, seq_lens, out)
+        if num_pages is None and isinstance(k_cache, int):
+            raise ValueError("num_pages is required when the caches are raw device addresses")
+        self._validate_caches(k_cache, v_cache, k_scale, v_scale, k_cache.shape[0] if num_pages is None else num_pages)
+        args = self.make_args(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, out, None,
+                              num_pages=num_pages)
+        _check("attn_run_static", lib().attn_run_static(self._handle, ctypes.byref(args), self._stream(stream)))
+        return out
 
     def _stream(self, stream):
         if stream is None:

@@ -115,6 +115,9 @@ struct attn_plan_s {
     size_t workspace_bytes;        // for desc.batch_capacity slots
 };
 
+// O(1) host checks of a call and its kernel parameter block (attn_plan.cpp).
+attn_status attn_prepare(attn_plan_t p, const attn_args* a, void* stream, attn::RunParams* rp);
+
 // Launchers implemented in attn_kernels.hip (host side of the HIP translation unit).
 attn_status attn_launch_split(const attn_plan_s* plan, const attn::RunParams& p, void* stream);
 attn_status attn_launch_combine(const attn_plan_s* plan, const attn::RunParams& p, void* stream);

@@ -34,6 +34,8 @@
 //    are bitwise reproducible and independent of the batch a request is in.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "attn_internal.h"
 
 namespace attn {
@@ -1109,4 +1111,56 @@ attn_status attn_stream_device(void* stream, int* device) {
     if (hipStreamGetDevice((hipStream_t)stream, &dev) != hipSuccess) return ATTN_E_HIP;
     *device = (int)dev;
     return ATTN_OK;
+}
+
+// ---- attn_run_static: the split workspace in a static device array ----
+
+// Device memory beyond the caller's buffers for callers that cannot allocate: the split panels of
+// attn_run_static. The HIP runtime places one copy on every GPU the library runs on, for the life
+// of the process. In host code this name is only a host-side stand-in: the array's device address
+// on each GPU comes from hipGetSymbolAddress, and only that address is ever passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[ATTN_STATIC_WORKSPACE_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices];       // device address of `scratch` per HIP ordinal
+
+// Device address of the static array on `device`, looked up once per device with that device
+// current (each GPU holds its own copy at its own address).
+attn_status scratch_address(int device, void** out) {
+    if (device < 0 || device >= kMaxScratchDevices) return ATTN_E_INVALID;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[device] == nullptr) {
+        int prev = -1;
+        if (hipGetDevice(&prev) != hipSuccess) return ATTN_E_HIP;
+        if (prev != device && hipSetDevice(device) != hipSuccess) return ATTN_E_HIP;
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (prev != device && hipSetDevice(prev) != hipSuccess) return ATTN_E_HIP;
+        if (e != hipSuccess || ptr == nullptr) return ATTN_E_HIP;
+        g_scratch_ptr[device] = ptr;
+    }
+    *out = g_scratch_ptr[device];
+    return ATTN_OK;
+}
+}  // namespace
+
+extern "C" attn_status attn_run_static(attn_plan_t p, const attn_args* a, void* stream) {
+    if (!p || !a) return ATTN_E_INVALID;
+    if (p->device == ATTN_DEVICE_HOST_ONLY) return ATTN_E_INVALID;
+    if (a->batch < 1 || a->batch > p->desc.batch_capacity) return ATTN_E_INVALID;
+    if (attn_plan_workspace_bytes(p, a->batch) > ATTN_STATIC_WORKSPACE_BYTES) return ATTN_E_STATIC_WORKSPACE;
+    void* ws = nullptr;
+    attn_status st = scratch_address(p->device, &ws);
+    if (st != ATTN_OK) return st;
+    attn_args local = *a;
+    local.workspace = ws;
+    local.workspace_bytes = ATTN_STATIC_WORKSPACE_BYTES;
+    attn::RunParams rp;
+    st = attn_prepare(p, &local, stream, &rp);
+    if (st != ATTN_OK) return st;
+    st = attn_launch_split(p, rp, stream);
+    if (st != ATTN_OK) return st;
+    return attn_launch_combine(p, rp, stream);
 }

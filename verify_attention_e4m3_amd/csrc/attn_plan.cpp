@@ -177,13 +177,14 @@ const char* attn_status_string(attn_status s) {
         case ATTN_E_UNSUPPORTED: return "unsupported geometry or dtype";
         case ATTN_E_HIP: return "HIP runtime error";
         case ATTN_E_WORKSPACE: return "workspace missing or too small";
+        case ATTN_E_STATIC_WORKSPACE: return "batch needs more workspace than the library's static array holds";
     }
     return "unknown status";
 }
 
 }  // extern "C"
 
-// Shared by attn_run / attn_combine: O(1) host checks, then the parameter block.
+// Shared by attn_run / attn_combine / attn_run_static: O(1) host checks, then the parameter block.
 attn_status attn_prepare(attn_plan_t p, const attn_args* a, void* stream, attn::RunParams* rp) {
     if (!p || !a || !rp) return ATTN_E_INVALID;
     if (p->device == ATTN_DEVICE_HOST_ONLY) return ATTN_E_INVALID;
