@@ -7,9 +7,16 @@ replay: "DFlash2 concurrent long-context attention", section "Attention-only mea
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
+Order of a run: inputs built in HBM; the split kernel event-timed until its launch time is steady
+(the GPU's clocks ramp up over the first few tens of launches after an idle moment; the first
+launches' time is reported under "cold_start"), then K more event-timed launches for the roofline;
+W warmup steps; exactly K timed steps (the reported value); the graph-replay protocol; streaming
+probes; the other synthetic configurations (default workload only); the CPU oracle baseline.
+
 Prints one JSON line: KV read GB/s (whole job), ms per layer, the roofline of the split kernel
-(HBM bytes it must read / its event-timed duration vs 8 TB/s), and the FP64 CPU oracle timed
-on a bounded sample of the same workload. With a long-prefill workload (--workload
+(HBM bytes it must read / its event-timed duration vs 8 TB/s), ms per layer and KV GB/s of the
+other synthetic configurations ("configs"), and the FP64 CPU oracle timed on a bounded sample of
+the same workload. With a long-prefill workload (--workload
 prefill_q8192_kv262144_hkv{1,2,4}) a step is one attn_prefill call and the line reports logical
 causal TFLOP/s against the FP16 MFMA peak instead.
 """
@@ -220,16 +227,145 @@ def bench_prefill(args, torch, A, wl):
     print(json.dumps(res))
 
 
+def verify_setup(torch, A, wl, w, dev, layers=None):
+    """Inputs, plan, workspace and argument blocks of one verify workload (all resident in HBM)."""
+    n_layers = layers or w.layers
+    cases = [wl.workload_case(w, device=dev, layer=i) for i in range(n_layers)]
+    c0 = cases[0]
+    plan = A.Plan(q_len=w.q_len, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                  page_size=w.page_size, max_seq_len=w.max_seq_len, max_pages_per_seq=c0["max_pages_per_seq"],
+                  batch_capacity=w.batch, kv_dtype=w.kv_format, device=dev)
+    ws = torch.empty(plan.workspace_bytes(w.batch) // 4, dtype=torch.float32, device=dev)
+    outs = [torch.empty_like(c["q"]) for c in cases]
+    arglist = [plan.make_args(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"], c["k_scale"],
+                              c["v_scale"], o, ws) for c, o in zip(cases, outs)]
+    lens = [int(x) for x in c0["seq_lens"].cpu().tolist()]
+    elem = wl.ELEMENT_BYTES[w.kv_format]
+    return dict(w=w, cases=cases, plan=plan, ws=ws, outs=outs, args=arglist, lens=lens, elem=elem,
+                kv_bytes=wl.kv_bytes(lens, w.num_kv_heads, w.head_dim, elem),
+                token_heads=sum(lens) * w.num_kv_heads, stream=torch.cuda.current_stream(dev))
+
+
+def step(env, i):
+    """One pass of the hot path over the batch: attn_run (split kernel) then attn_combine."""
+    a = env["args"][i % len(env["args"])]
+    env["plan"].split(a)
+    env["plan"].combine(a)
+
+
+def event_split_ms(torch, env, n, first=0):
+    """n steps with HIP events around every split-kernel launch, on the stream it is launched on;
+    returns the split kernel's durations in ms."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        a = env["args"][(first + i) % len(env["args"])]
+        ev[i][0].record(env["stream"])
+        env["plan"].split(a)
+        ev[i][1].record(env["stream"])
+        env["plan"].combine(a)
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in ev]
+
+
+def settled_split_ms(torch, env, k, window=16, min_windows=3, max_windows=20, tol=0.015):
+    """The split kernel's per-launch duration once it is steady. After the GPU has idled (0.2 s is
+    enough) its clocks ramp up over the first few tens of launches of this load, and early launches
+    run up to a quarter slower; windows of event-timed launches run until two consecutive window
+    means agree within tol, then k more launches are timed. Returns (k durations, cold-start record)."""
+    step(env, 0)                 # the first launch also loads the kernels' code object
+    torch.cuda.synchronize()
+    means = []
+    done = 1
+    for wdx in range(max_windows):
+        ms = event_split_ms(torch, env, window, first=done)
+        done += window
+        means.append(statistics.fmean(ms))
+        if wdx + 1 >= min_windows and abs(means[-1] - means[-2]) <= tol * means[-1]:
+            break
+    timed = event_split_ms(torch, env, k, first=done)
+    cold = {"first_window_split_ms": round(means[0], 5), "settled_split_ms": round(statistics.fmean(timed), 5),
+            "launches_to_settle": done, "window": window}
+    return timed, cold
+
+
+def timed_region(torch, env, steps, warmup):
+    """W untimed warmup steps, then exactly K steps bracketed by device synchronisation; ms per step."""
+    for i in range(warmup):
+        step(env, i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(env, warmup + i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def graph_protocol(torch, env, layers=None, replays=8, samples=5):
+    """The pages' protocol: one graph over the per-layer working sets, `replays` replays per sample,
+    median of `samples` samples; ms per layer."""
+    n = layers or len(env["args"])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            step(env, i)
+    g.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(samples):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(replays):
+            g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        out.append(s.elapsed_time(e) / (replays * n))
+    del g
+    return out
+
+
+# The other synthetic configurations of the benchmark recipe, timed in the same process as the
+# headline: (workload, label). Each cycles its own per-layer caches.
+OTHER_CONFIGS = [
+    ("verify_b1_ctx3297_hq6_hkv1", "B1 x 3297, q8, Hq6/Hkv1, E4M3 D256, page 1648 (latency-bound)"),
+    ("verify_b4_ctx32k_gqa6", "B4 x 32768, q8, Hq24/Hkv4, E4M3 D256 (0.5 N(0,1), scales 2.0), page 1648"),
+    ("verify_b16_mixed_ctx256k_page3296", "B16 mixed lengths <= 262144 (2 zero rows, 3 padded slots), q8, "
+                                          "Hq24/Hkv4, E4M3 D256, page 3296"),
+    ("decode_b8_ctx32k_d128_fp16_gqa4", "B8 x 32768, q1, Hq32/Hkv8 (GQA4), FP16 KV D128, page 1648"),
+]
+
+
+def other_configs(torch, A, wl, dev, steps=64, warmup=16):
+    """ms per layer, KV GB/s and the fraction of 8 TB/s of every other synthetic configuration."""
+    res = {}
+    for name, label in OTHER_CONFIGS:
+        w = wl.WORKLOADS[name]
+        env = verify_setup(torch, A, wl, w, dev)
+        split_ms, cold = settled_split_ms(torch, env, 32)
+        ms = timed_region(torch, env, steps, warmup)
+        graph = graph_protocol(torch, env)
+        kvb = env["kv_bytes"]
+        res[name] = {"label": label, "kv_bytes_per_layer": kvb, "ms_per_layer": round(ms, 5),
+                     "kv_gbs": round(kvb / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(kvb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "split_ms_mean": round(statistics.fmean(split_ms), 5),
+                     "graph_ms_per_layer_median": round(statistics.median(graph), 5),
+                     "graph_kv_gbs": round(kvb / (statistics.median(graph) * 1e-3) / 1e9, 1),
+                     "steps": steps, "warmup": warmup, "layers": len(env["args"])}
+        del env
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128)
-    # The GPU needs about 40 ms of this load before its clocks settle: with 16 warmup steps the
-    # timed region still runs about 6% slow.
-    ap.add_argument("--warmup", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip timing the other synthetic configurations")
     args = ap.parse_args()
     args.steps_given = any(a.startswith("--steps") for a in sys.argv[1:])
     args.warmup_given = any(a.startswith("--warmup") for a in sys.argv[1:])
@@ -251,19 +387,9 @@ def main():
     if args.workload in wl.PREFILL_WORKLOADS:
         return bench_prefill(args, torch, A, wl)
     w = wl.WORKLOADS[args.workload]
-    layers = [wl.workload_case(w, device=dev, layer=i) for i in range(w.layers)]
-    c0 = layers[0]
-    plan = A.Plan(q_len=w.q_len, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
-                  page_size=w.page_size, max_seq_len=w.max_seq_len, max_pages_per_seq=c0["max_pages_per_seq"],
-                  batch_capacity=w.batch, kv_dtype=w.kv_format, device=dev)
-    ws = torch.empty(plan.workspace_bytes(w.batch) // 4, dtype=torch.float32, device=dev)
-    outs = [torch.empty_like(c["q"]) for c in layers]
-    arglist = [plan.make_args(c["q"], c["k_cache"], c["v_cache"], c["block_table"], c["seq_lens"], c["k_scale"],
-                              c["v_scale"], o, ws) for c, o in zip(layers, outs)]
-    elem = wl.ELEMENT_BYTES[w.kv_format]
-    lens = [int(x) for x in c0["seq_lens"].cpu().tolist()]
-    kv_bytes = wl.kv_bytes(lens, w.num_kv_heads, w.head_dim, elem)
-    token_heads = sum(lens) * w.num_kv_heads
+    env = verify_setup(torch, A, wl, w, dev)
+    plan, lens, kv_bytes, token_heads, elem = env["plan"], env["lens"], env["kv_bytes"], env["token_heads"], env["elem"]
+    c0 = env["cases"][0]
     # split_kernel<format, row tiles, KV heads per workgroup>: format 0 = E4M3 D256, 1 = FP16 D128,
     # 2 = E5M2 D256, 3 = FP16 D256, 4 = E4M3 D128; 16 packed rows per tile; a workgroup holds the
     # largest group of KV heads (up to 4 for E4M3 D128, 2 otherwise) that divides Hkv while the
@@ -277,75 +403,35 @@ def main():
             break
     kernel_name = f"split_kernel<{fmt}, {-(-plan.info['rows'] // 16)}, {hp}>"
 
-    def step(i):
-        a = arglist[i % w.layers]
-        plan.split(a)
-        plan.combine(a)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # Timed region: exactly K steps (split + combine per step), eager on the work stream,
-    # bracketed by device synchronisation. Nothing else is enqueued in between.
-    stream = torch.cuda.current_stream(dev)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-
-    # The same K steps again with HIP events around every split-kernel launch, on the stream
-    # the kernels are launched on: the split kernel's own average duration for the roofline.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        a = arglist[i % w.layers]
-        ev[i][0].record(stream)
-        plan.split(a)
-        ev[i][1].record(stream)
-        plan.combine(a)
-    torch.cuda.synchronize()
-    split_ms = [s.elapsed_time(e) for s, e in ev]
+    # The split kernel's own duration for the roofline: HIP events around every split launch on its
+    # stream, taken once the launch time is steady (events add dispatch gaps, so they stay out of the
+    # timed region). This pass also brings the GPU's clocks to their loaded state before the timed
+    # region; how slow the first launches were is reported under "cold_start".
+    split_ms, cold = settled_split_ms(torch, env, args.steps)
     split_ms_mean = statistics.fmean(split_ms)
     achieved = kv_bytes / (split_ms_mean * 1e-3) / 1e9
 
+    # Timed region: W warmup steps, then exactly K steps (split + combine per step), eager on the
+    # work stream, bracketed by device synchronisation. Nothing else is enqueued in between.
+    ms_per_step = timed_region(torch, env, args.steps, args.warmup)
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+
     graph = None
     if not args.no_graph:
-        # The pages' protocol: one graph over the per-layer working sets, 8 replays per sample,
-        # median of 5 samples.
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(w.layers):
-                step(i)
-        g.replay()
-        torch.cuda.synchronize()
-        samples = []
-        for _ in range(5):
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
-            for _ in range(8):
-                g.replay()
-            e.record()
-            torch.cuda.synchronize()
-            samples.append(s.elapsed_time(e) / (8 * w.layers))
+        samples = graph_protocol(torch, env)
         graph = {"ms_per_layer_median": round(statistics.median(samples), 5),
                  "ms_per_layer_min": round(min(samples), 5), "ms_per_layer_max": round(max(samples), 5),
                  "kv_gbs_median": round(kv_bytes / (statistics.median(samples) * 1e-3) / 1e9, 1)}
-        del g
 
         # The bounded-graph set: host selector on the CPU length hints, copies of the live batch
         # into its static buffers, one replay of its graph over all layers. Every layer uses
         # layer 0's block table and lengths here (the per-layer caches hold the same page pool),
         # as the layers of one model share their requests.
         from verify_attention_e4m3_amd.graphs import LayerCache, VerifyGraphs
-        gset = VerifyGraphs(plan, [LayerCache(c["k_cache"], c["v_cache"], c["k_scale"], c["v_scale"]) for c in layers],
-                            batch_sizes=(w.batch,), bank=A.WorkspaceBank())
+        gset = VerifyGraphs(plan, [LayerCache(c["k_cache"], c["v_cache"], c["k_scale"], c["v_scale"])
+                                   for c in env["cases"]], batch_sizes=(w.batch,), bank=A.WorkspaceBank())
         gset.capture()
-        qs = [c["q"] for c in layers]
+        qs = [c["q"] for c in env["cases"]]
         _, route = gset.run(qs, c0["block_table"], c0["seq_lens"], lens)
         torch.cuda.synchronize()
         samples = []
@@ -392,6 +478,7 @@ def main():
                      "kernel": kernel_name, "split_ms_mean": round(split_ms_mean, 5),
                      "algorithmic_bytes_per_launch": kv_bytes, "units_per_launch": token_heads,
                      "bytes_per_unit": 2 * w.head_dim * elem},
+        "cold_start": cold,
         "graph_replay": graph,
         "copy_probe_gbs": round(copy_gbs, 1),
         "read_probe_gbs": round(read_gbs, 1),
@@ -400,6 +487,11 @@ def main():
         "split_ms_p10_p50_p90": [round(x, 5) for x in statistics.quantiles(split_ms, n=10)[0::4]],
     }
     res["run"] = run_context(torch, dev)
+    if not args.no_configs and w.name == DEFAULT_WORKLOAD:
+        del env
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        res["configs"] = other_configs(torch, A, wl, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, c0)
     print(json.dumps(res))

@@ -49,10 +49,12 @@ class Workload:
 
 WORKLOADS = {
     w.name: w for w in [
-        Workload("verify_b1_ctx3297_hq6_hkv1", 1, 3297, 8, 6, 1, 256, 1648, "e4m3", 1.0, 1.0, 1, 1, 4096,
-                 "B1, seq_len 3297 incl. 8 new tokens, Hq6/Hkv1, page 1648, pages from a 64-page pool"),
-        Workload("verify_b4_ctx32k_gqa6", 4, 32768, 8, 24, 4, 256, 1648, "e4m3", 0.5, 2.0, 1, 2, 32768,
-                 "B4 x 32768, Hq24/Hkv4, E4M3 of 0.5*N(0,1) with k/v scales 2.0, shuffled pages"),
+        Workload("verify_b1_ctx3297_hq6_hkv1", 1, 3297, 8, 6, 1, 256, 1648, "e4m3", 1.0, 1.0, 16, 1, 4096,
+                 "B1, seq_len 3297 incl. 8 new tokens, Hq6/Hkv1, page 1648, pages from a 64-page pool, "
+                 "16 per-layer caches"),
+        Workload("verify_b4_ctx32k_gqa6", 4, 32768, 8, 24, 4, 256, 1648, "e4m3", 0.5, 2.0, 8, 2, 32768,
+                 "B4 x 32768, Hq24/Hkv4, E4M3 of 0.5*N(0,1) with k/v scales 2.0, shuffled pages, "
+                 "8 per-layer caches (2.1 GB, beyond the memory-side cache)"),
         Workload("verify_b8_ctx128k_gqa6_16layers", 8, 131072, 8, 24, 4, 256, 1648, "e4m3", 1.0, 1.0, 16, 3,
                  131072, "B8 x 131072, Hq24/Hkv4, 16 independent per-layer caches, shuffled pages"),
         Workload("verify_b16_mixed_ctx256k_page3296", 16, None, 8, 24, 4, 256, 3296, "e4m3", 1.0, 1.0, 1, 4,
