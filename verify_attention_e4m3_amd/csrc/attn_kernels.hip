@@ -155,6 +155,9 @@ struct Fmt8D256 {
     static constexpr int KSTEPS = 8;
     static constexpr int JT = 16;
     static constexpr int TILE = 32, NG = 2, B_TOK = 16, B_BYTES = 0, ROW = 256;
+    // V^T operands come from transposed LDS reads (see read_v); PV accumulator element i of
+    // tile j holds dim 16*j + 4*qd + i, so the four elements of a tile are consecutive dims.
+    static constexpr bool VTR = true;
     typedef half8 PopT;
     template <int RT>
     __device__ static void qk(const TileK& t, float4v (&sacc)[2][RT], const half8 (&qop)[RT][KSTEPS]) {
@@ -165,32 +168,17 @@ struct Fmt8D256 {
         const u32x4 w = k[ks >> 1];
         return (ks & 1) ? Dec::x8(w[2], w[3]) : Dec::x8(w[0], w[1]);
     }
-    __device__ static int o_dim(int qd, int i, int j) { return 16 * (4 * qd + i) + j; }
-    // O^T += V^T . P^T. For dword w of the lane's 16 V bytes and byte pair (2cp, 2cp+1), tokens
-    // (2pp, 2pp+1) of dims 16*n + 4*w + 2*cp + {0,1} become the FP16 pairs of the A operand.
+    __device__ static int o_dim(int qd, int i, int j) { return 16 * j + 4 * qd + i; }
+    // O^T += V^T . P^T. Dwords 2*(j%2) and 2*(j%2)+1 of t.v[j/2] hold dim 16*j + lane%16 of the
+    // lane's 8 tokens in k order (read_v), so one decode gives MFMA j's A operand.
     template <int RT>
     __device__ static void pv(const TileV& t, const half8 (&pop)[RT], float4v (&o)[RT][JT]) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int j = 0; j < JT; ++j) {
+            const half8 a = Dec::x8(t.v[j >> 1][2 * (j & 1)], t.v[j >> 1][2 * (j & 1) + 1]);
 #pragma unroll
-            for (int cp = 0; cp < 2; ++cp) {
-                half8 a0, a1;
-#pragma unroll
-                for (int pp = 0; pp < 4; ++pp) {
-                    half2v lo, hi;
-                    Dec::pair(t.v[2 * pp + 1][w], t.v[2 * pp][w], cp, lo, hi);
-                    a0[2 * pp] = lo[0];
-                    a0[2 * pp + 1] = lo[1];
-                    a1[2 * pp] = hi[0];
-                    a1[2 * pp + 1] = hi[1];
-                }
-                const int jd = 4 * w + 2 * cp;
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    o[rt][jd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, pop[rt], o[rt][jd], 0, 0, 0);
-                    o[rt][jd + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, pop[rt], o[rt][jd + 1], 0, 0, 0);
-                }
-            }
+            for (int rt = 0; rt < RT; ++rt)
+                o[rt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pop[rt], o[rt][j], 0, 0, 0);
         }
     }
 };
@@ -206,6 +194,7 @@ template <> struct Fmt<kFmtF16D128> {
     static constexpr int KSTEPS = 4;
     static constexpr int JT = 8;
     static constexpr int TILE = 32, NG = 2, B_TOK = 16, B_BYTES = 0, ROW = 256;
+    static constexpr bool VTR = false;
     typedef half8 PopT;
     template <int RT>
     __device__ static void qk(const TileK& t, float4v (&sacc)[2][RT], const half8 (&qop)[RT][KSTEPS]) {
@@ -247,6 +236,7 @@ template <> struct Fmt<kFmtF16D256> {
     static constexpr int KSTEPS = 8;
     static constexpr int JT = 16;
     static constexpr int TILE = 16, NG = 1, B_TOK = 0, B_BYTES = 256, ROW = 256;
+    static constexpr bool VTR = false;
     typedef half4 PopT;
     __device__ static int q_dim(int ks, int qd) { return 32 * ks + 8 * qd; }
     __device__ static int o_dim(int qd, int i, int j) { return j < 8 ? 8 * (4 * qd + i) + j : 128 + 8 * (4 * qd + i) + j - 8; }
@@ -294,6 +284,7 @@ template <> struct Fmt<kFmtE4M3D128> {
     static constexpr int KSTEPS = 4;
     static constexpr int JT = 8;
     static constexpr int TILE = 32, NG = 2, B_TOK = 16, B_BYTES = 0, ROW = 128;
+    static constexpr bool VTR = false;
     typedef half8 PopT;
     __device__ static int q_dim(int ks, int qd) { return 64 * (ks >> 1) + 16 * qd + 8 * (ks & 1); }
     __device__ static half8 k_op(const u32x4 (&k)[4], int ks) {
@@ -356,7 +347,13 @@ struct Geo {
     __device__ static int swz(int t) { return F::ROW == 256 ? t : (t >> 1); }
     static constexpr int KLOADS = 2 * KL;             // per tile and wave
     static constexpr int VLOADS = 2 * KL;             // V is stored once, like K
-    static constexpr int STAGE = (KLOADS + VLOADS) * 1024;
+    // V load e of a tile lands at vblk(e) bytes from the stage's V region. For transposed V
+    // reads the blocks are 1040 bytes apart, so each block's token rows start 16 bytes further
+    // along the LDS banks than the previous block's and the eight rows a 16-lane group reads
+    // together (one per block) fall on eight different bank groups.
+    static constexpr int VBLK = F::VTR ? 1040 : 1024;
+    __device__ static constexpr int vblk(int e) { return VBLK * e; }
+    static constexpr int STAGE = KLOADS * 1024 + (F::VTR ? VLOADS * 1040 + 128 : VLOADS * 1024);
     static constexpr int VROW = KLOADS;               // first 1 KB row of V in a stage
     static constexpr int NS = 2;                      // ring stages per wave
     static constexpr int RING = NS * STAGE;           // ring bytes per wave
@@ -381,8 +378,9 @@ __device__ __forceinline__ void locate(int32_t j, const RunParams& p, int32_t& p
 //    fetches 16-byte chunk (l%16) ^ (token%16) of its row into LDS slot l%16. The XOR swizzle
 //    lets the MFMA-order reads of the consumer (16 lanes = 16 tokens, same chunk) hit 16
 //    different LDS bank groups.
-// V: slot e of lane (n, qd) is token 4*qd + (e&3) of granule e>>2, dims 16*n + 0..15 - the
-//    lane that loads a chunk is the lane that consumes it.
+// V: load e (0..3) of a granule covers tokens 4*q + e of it, quarter q of the load being token
+//    4*q + e's row; lane (n, qd) fetches dims 16*n + 0..15 of token 4*qd + e. Without transposed
+//    reads the lane that loads a chunk is the lane that consumes it (read_v).
 struct LaneOffs {
     uint32_t k[4];
     uint32_t v[4];
@@ -502,8 +500,8 @@ __device__ __forceinline__ void issue_v(const Granules& gr, int32_t last, const 
     if (gr.j0 + F::TILE - 1 <= last && !gr.past_end) {
 #pragma unroll
         for (int e = 0; e < VPG; ++e) {
-            dma16(gr.vA, lo.v[e], v0 + e * 1024);
-            dma16(gr.vB, lo.v[e], v0 + (VPG + e) * 1024);
+            dma16(gr.vA, lo.v[e], v0 + G::vblk(e));
+            dma16(gr.vB, lo.v[e], v0 + G::vblk(VPG + e));
         }
     } else {
         // 256-byte rows: lane (n, qd) loads dims 16n.. of tokens 4qd + e; 128-byte rows: lane l
@@ -515,21 +513,40 @@ __device__ __forceinline__ void issue_v(const Granules& gr, int32_t last, const 
             const uint32_t oa = (uint32_t)((min(gr.j0 + rel, last) - gr.j0) * p.v_token_stride + vb);
             const uint32_t ob = (uint32_t)((min(gr.j0 + F::B_TOK + rel, last) - gr.gsB) * p.v_token_stride + vb);
             const uint32_t oz = (uint32_t)((last - gr.j0) * p.v_token_stride + vb);
-            dma16(gr.vA, gr.past_end ? oz : oa, v0 + e * 1024);
-            dma16(gr.vB, gr.past_end ? oz : ob, v0 + (VPG + e) * 1024);
+            dma16(gr.vA, gr.past_end ? oz : oa, v0 + G::vblk(e));
+            dma16(gr.vB, gr.past_end ? oz : ob, v0 + G::vblk(VPG + e));
         }
     }
 }
 
-// The V operand of a tile from its ring stage: slot e of lane (n, qd) is token 4*qd + (e&3) of
-// granule e>>2. 256-byte rows: its 16 bytes of dims 16n.., stored by this very lane. 128-byte
-// rows: the 8 bytes of dims 8n.. (in v[e][0..1]), from where issue_v placed that token's row.
+// The V operand of a tile from its ring stage. V load e (block vblk(e)) holds, in its quarter q
+// (256 bytes), the row of token 4*q + (e&3) of granule e>>2.
+//  * Transposed reads (one-byte formats at D = 256): for PV tile j (dims 16*j ..), 16-lane group
+//    qd needs its 8 tokens 4*qd + (r&3) of granule r>>2 (r = 0..7, the order P holds them) for
+//    every dim of the tile. ds_read_b64_tr_b8 takes, in each 16-lane group, an 8 x 16 byte
+//    block whose row r is the 8-byte pieces of lanes 2r and 2r+1, and gives lane n column n:
+//    so lane n points at row n/2 = block n/2, quarter qd, bytes 16*j + 8*(n&1). Slot j of the
+//    result holds dim 16*j + n of those tokens in k order (dwords 2*(j&1), 2*(j&1)+1 of v[j/2]).
+//  * 256-byte rows otherwise: slot e of lane (n, qd) is the 16 bytes of dims 16n.. of token
+//    4*qd + (e&3) of granule e>>2, stored by this very lane.
+//  * 128-byte rows: the 8 bytes of dims 8n.. (in v[e][0..1]), from where issue_v placed that
+//    token's row.
 template <class F>
 __device__ __forceinline__ TileV read_v(const uint8_t* stage, int n, int qd, int lane) {
     using G = Geo<F>;
     TileV tv;
     const uint8_t* v0 = stage + G::VROW * 1024;
-    if constexpr (F::ROW == 256) {
+    if constexpr (F::VTR) {
+        typedef int int2v __attribute__((ext_vector_type(2)));
+        const uint8_t* base = v0 + G::vblk(n >> 1) + 256 * qd + 8 * (n & 1);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int2v w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) int2v*)(__attribute__((address_space(3))) const void*)(base + 16 * j));
+            tv.v[j >> 1][2 * (j & 1)] = (uint32_t)w[0];
+            tv.v[j >> 1][2 * (j & 1) + 1] = (uint32_t)w[1];
+        }
+    } else if constexpr (F::ROW == 256) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) tv.v[e] = *reinterpret_cast<const u32x4*>(v0 + e * 1024 + 16 * lane);
     } else {
@@ -568,11 +585,12 @@ __device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt
 // Softmax step of one tile: masked raw scores (lane holds row n's tokens j0 + 16*tt + 4*qd + i of
 // the NG granules of scores), exponentials exp2(c*x - m) against the row references (c > 0,
 // log2 units), P^T in FP16. Returns true (uniformly) when a row's tile max exceeds its reference
-// by more than kRefSlack; the references are then raised and nothing was accumulated.
+// by more than kRefSlack; the references are then raised and nothing was accumulated. The row
+// sums of P are taken by row_sums, from the FP16 P that the PV product uses.
 template <int RT, int NG, int TILE, class PopT>
 __device__ __forceinline__ bool softmax_tile(const float4v (&sacc)[2][RT], int32_t j0, int32_t mask_from,
                                              const int32_t (&lim)[RT], float c, float (&m_ref)[RT],
-                                             float (&l_run)[RT], PopT (&pop)[RT], int qd) {
+                                             PopT (&pop)[RT], int qd) {
     constexpr int NV = 4 * NG;
     float x[RT][NV];
 #pragma unroll
@@ -611,16 +629,26 @@ __device__ __forceinline__ bool softmax_tile(const float4v (&sacc)[2][RT], int32
     for (int rt = 0; rt < RT; ++rt) {
         if (m_ref[rt] == -INFINITY) m_ref[rt] = mx[rt];        // first tile with a visible key
         const float neg_m = m_ref[rt] == -INFINITY ? 0.0f : -m_ref[rt];
-        float pe[NV];
 #pragma unroll
-        for (int e = 0; e < NV; ++e) pe[e] = fast_exp2(__builtin_fmaf(x[rt][e], c, neg_m));
-        float sum = (pe[0] + pe[1]) + (pe[2] + pe[3]);
-        if constexpr (NV == 8) sum += (pe[4 % NV] + pe[5 % NV]) + (pe[6 % NV] + pe[7 % NV]);
-        l_run[rt] += sum;
-#pragma unroll
-        for (int e = 0; e < NV; ++e) pop[rt][e] = (_Float16)pe[e];
+        for (int e = 0; e < NV; ++e) pop[rt][e] = (_Float16)fast_exp2(__builtin_fmaf(x[rt][e], c, neg_m));
     }
     return false;
+}
+
+// Row sums of a tile's P on the matrix cores: a 16 x K block of ones times P^T (K tokens x 16 rows)
+// adds, in every element of lane (n, qd)'s accumulator, the sum of packed row n's K weights - one
+// MFMA per row tile instead of a VALU add tree, over the same FP16 weights the PV product uses.
+template <int RT>
+__device__ __forceinline__ void row_sums(const half8 (&pop)[RT], float4v (&lsum)[RT]) {
+    const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) lsum[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop[rt], lsum[rt], 0, 0, 0);
+}
+template <int RT>
+__device__ __forceinline__ void row_sums(const half4 (&pop)[RT], float4v (&lsum)[RT]) {
+    const half4 ones = {1, 1, 1, 1};
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) lsum[rt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pop[rt], lsum[rt], 0, 0, 0);
 }
 
 // Exact maximum of every row's scaled, masked scores over the split (log2 units; -inf for a
@@ -819,13 +847,13 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>(
     // over the split as its reference (then no tile can exceed it). Both passes depend only on
     // the split's own data, so the result is deterministic.
     float m_ref[RT];
-    float l_run[RT];
+    float4v lsum[RT];        // row sums of P: every element of lane (n, qd) holds packed row n's
     float4v o[RT][JT];
 
     auto run_pass = [&]() -> bool {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            l_run[rt] = 0.0f;
+            lsum[rt] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < JT; ++j) o[rt][j] = float4v{0.f, 0.f, 0.f, 0.f};
         }
@@ -862,9 +890,10 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>(
             issue_v<F>(gn, last, lo, stage, p, n, qd, lane);
             gn = granules<F>(j0 + (G::NS + 1) * kStride, last, pages, pg0, kbase, vbase, p);
             typename F::PopT pop[RT];
-            over = softmax_tile<RT, F::NG, F::TILE>(sacc, j0, mask_from, lim, c, m_ref, l_run, pop, qd);
+            over = softmax_tile<RT, F::NG, F::TILE>(sacc, j0, mask_from, lim, c, m_ref, pop, qd);
             if (over) break;
             F::template pv<RT>(tv, pop, o);
+            row_sums<RT>(pop, lsum);
             j0 += kStride;
             if (j0 > last) break;
         }
@@ -880,7 +909,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>(
     }
 
     // Hand-over: each head's second wave writes its accumulators (element i of O^T tile (rt, j)
-    // as row (rt*JT + j)*4 + i of 64 lanes), its references and its lane-partial sums into the
+    // as row (rt*JT + j)*4 + i of 64 lanes), its references and its row sums into the
     // head's region of the rings; the first wave reads the same lane's values back, so both
     // sides are conflict-free.
     constexpr int kXferFloats = (RT * JT * 4 + 2 * RT) * 64;
@@ -895,15 +924,15 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) xfer[((rt * JT + j) * 4 + i) * 64 + lane] = o[rt][j][i];
             xfer[(RT * JT * 4 + rt) * 64 + lane] = m_ref[rt];
-            xfer[(RT * JT * 4 + RT + rt) * 64 + lane] = l_run[rt];
+            xfer[(RT * JT * 4 + RT + rt) * 64 + lane] = lsum[rt][0];
         }
     }
     __syncthreads();
     if (half == 1) return;
 
     // Merge (first wave, then second) and write the head's split panel: O^T tile j holds
-    // O[row n][dim F::o_dim(qd, i, j)] in element i; for a fixed i, groups of 4 consecutive j
-    // are 4 consecutive dims.
+    // O[row n][dim F::o_dim(qd, i, j)] in element i; the four elements of a tile (transposed V
+    // reads) or, for a fixed i, groups of 4 consecutive j (otherwise) are 4 consecutive dims.
     const int rows_alloc = 16 * RT;
     float* panel = p.ws + ((int64_t)(b * p.num_kv_heads + g) * p.grid_splits + s) * p.split_floats;
 #pragma unroll
@@ -916,21 +945,30 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>(
         const float a1 = m1 == -INFINITY ? 0.0f : fast_exp2(m1 - M);
         const int r = rt * 16 + n;
         float* orow = panel + r * D;
+        if constexpr (F::VTR) {
+            // the four elements of a tile are four consecutive dims
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int c4 = 0; c4 < JT / 4; ++c4) {
+            for (int j = 0; j < JT; ++j) {
                 float4v v;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int j = 4 * c4 + u;
-                    v[u] = a0 * o[rt][j][i] + a1 * xfer[((rt * JT + j) * 4 + i) * 64 + lane];
-                }
-                *reinterpret_cast<float4v*>(orow + F::o_dim(qd, i, 4 * c4)) = v;
+                for (int i = 0; i < 4; ++i) v[i] = a0 * o[rt][j][i] + a1 * xfer[((rt * JT + j) * 4 + i) * 64 + lane];
+                *reinterpret_cast<float4v*>(orow + F::o_dim(qd, 0, j)) = v;
             }
-        float l = a0 * l_run[rt] + a1 * l1;
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int c4 = 0; c4 < JT / 4; ++c4) {
+                    float4v v;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int j = 4 * c4 + u;
+                        v[u] = a0 * o[rt][j][i] + a1 * xfer[((rt * JT + j) * 4 + i) * 64 + lane];
+                    }
+                    *reinterpret_cast<float4v*>(orow + F::o_dim(qd, i, 4 * c4)) = v;
+                }
+        }
+        const float l = a0 * lsum[rt][0] + a1 * l1;
         if (qd == 0) {
             panel[rows_alloc * D + r] = M;
             panel[rows_alloc * D + rows_alloc + r] = l;
