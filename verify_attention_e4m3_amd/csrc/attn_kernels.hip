@@ -284,47 +284,29 @@ template <> struct Fmt<kFmtE4M3D128> {
     static constexpr int KSTEPS = 4;
     static constexpr int JT = 8;
     static constexpr int TILE = 32, NG = 2, B_TOK = 16, B_BYTES = 0, ROW = 128;
-    static constexpr bool VTR = false;
+    // V^T operands from transposed LDS reads, as for the one-byte D = 256 formats (read_v).
+    static constexpr bool VTR = true;
     typedef half8 PopT;
     __device__ static int q_dim(int ks, int qd) { return 64 * (ks >> 1) + 16 * qd + 8 * (ks & 1); }
     __device__ static half8 k_op(const u32x4 (&k)[4], int ks) {
         const u32x4 w = k[ks >> 1];
         return (ks & 1) ? e4m3x8(w[2], w[3]) : e4m3x8(w[0], w[1]);
     }
-    __device__ static int o_dim(int qd, int i, int j) { return 8 * (4 * qd + i) + j; }
+    __device__ static int o_dim(int qd, int i, int j) { return 16 * j + 4 * qd + i; }
     template <int RT>
     __device__ static void qk(const TileK& t, float4v (&sacc)[2][RT], const half8 (&qop)[RT][KSTEPS]) {
         qk_two_granules<Fmt<kFmtE4M3D128>, RT>(t, sacc, qop);
     }
+    // O^T += V^T . P^T: slot j of the transposed read holds dim 16*j + lane%16 of the lane's 8
+    // tokens in k order.
     template <int RT>
     __device__ static void pv(const TileV& t, const half8 (&pop)[RT], float4v (&o)[RT][JT]) {
-        uint32_t dw[8][2];                           // slot e: this lane's 8 dims (8 bytes) of one token
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            dw[e][0] = t.v[e][0];
-            dw[e][1] = t.v[e][1];
-        }
+        for (int j = 0; j < JT; ++j) {
+            const half8 a = e4m3x8(t.v[j >> 1][2 * (j & 1)], t.v[j >> 1][2 * (j & 1) + 1]);
 #pragma unroll
-        for (int w = 0; w < 2; ++w) {
-#pragma unroll
-            for (int cp = 0; cp < 2; ++cp) {
-                half8 a0, a1;
-#pragma unroll
-                for (int pp = 0; pp < 4; ++pp) {
-                    half2v lo, hi;
-                    DecE4M3::pair(dw[2 * pp + 1][w], dw[2 * pp][w], cp, lo, hi);
-                    a0[2 * pp] = lo[0];
-                    a0[2 * pp + 1] = lo[1];
-                    a1[2 * pp] = hi[0];
-                    a1[2 * pp + 1] = hi[1];
-                }
-                const int jd = 4 * w + 2 * cp;
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    o[rt][jd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, pop[rt], o[rt][jd], 0, 0, 0);
-                    o[rt][jd + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, pop[rt], o[rt][jd + 1], 0, 0, 0);
-                }
-            }
+            for (int rt = 0; rt < RT; ++rt)
+                o[rt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pop[rt], o[rt][j], 0, 0, 0);
         }
     }
 };
@@ -357,11 +339,11 @@ struct Geo {
     static constexpr int VROW = KLOADS;               // first 1 KB row of V in a stage
     static constexpr int NS = 2;                      // ring stages per wave
     static constexpr int RING = NS * STAGE;           // ring bytes per wave
-    // 128-byte rows, V: load instruction e of a granule holds its tokens 8e + vtok(r) in 128-byte
-    // row r, so that the tokens 4 apart that a half wave reads together sit in adjacent 128-byte
-    // rows (other LDS banks): r = 2b + a holds token 4a + b.
-    __device__ static int vtok(int r) { return 4 * (r & 1) + (r >> 1); }
-    __device__ static int vrow(int t) { return 2 * (t & 3) + ((t >> 2) & 1); }
+    // 128-byte rows, V: load p (0, 1) of a granule holds, in its 128-byte row q, the granule's
+    // token 4*(q/2) + 2*(q%2) + p: the 4 tokens a 16-lane group takes from a granule (4*qd + i,
+    // i = 0..3) lie in two loads (i & 1) and two row parities (i >> 1), which with the loads'
+    // 16-byte phase steps puts the group's 8 rows on 8 different bank groups.
+    __device__ static int vtok128(int q, int p) { return 4 * (q >> 1) + 2 * (q & 1) + p; }
 };
 
 // Page and slot of logical token j (a granule start): j / page_size by a multiply-shift with
@@ -401,7 +383,7 @@ __device__ __forceinline__ LaneOffs lane_offsets(const RunParams& p, int lane, i
         for (int e = 0; e < 4; ++e) o.v[e] = (uint32_t)((4 * qd + e) * p.v_token_stride + 16 * n);
     } else {
 #pragma unroll
-        for (int e = 0; e < 2; ++e) o.v[e] = (uint32_t)((8 * e + G::vtok(lane >> 3)) * p.v_token_stride + 16 * (lane & 7));
+        for (int e = 0; e < 2; ++e) o.v[e] = (uint32_t)(G::vtok128(lane >> 3, e) * p.v_token_stride + 16 * (lane & 7));
         o.v[2] = o.v[3] = 0;
     }
     return o;
@@ -505,11 +487,11 @@ __device__ __forceinline__ void issue_v(const Granules& gr, int32_t last, const 
         }
     } else {
         // 256-byte rows: lane (n, qd) loads dims 16n.. of tokens 4qd + e; 128-byte rows: lane l
-        // loads chunk l % 8 of token 8e + vtok(l / 8).
+        // loads chunk l % 8 of token vtok128(l / 8, e).
         const uint32_t vb = F::ROW == 256 ? 16 * n : 16 * (lane & 7);
 #pragma unroll
         for (int e = 0; e < VPG; ++e) {
-            const int rel = F::ROW == 256 ? 4 * qd + e : 8 * e + G::vtok(lane >> 3);
+            const int rel = F::ROW == 256 ? 4 * qd + e : G::vtok128(lane >> 3, e);
             const uint32_t oa = (uint32_t)((min(gr.j0 + rel, last) - gr.j0) * p.v_token_stride + vb);
             const uint32_t ob = (uint32_t)((min(gr.j0 + F::B_TOK + rel, last) - gr.gsB) * p.v_token_stride + vb);
             const uint32_t oz = (uint32_t)((last - gr.j0) * p.v_token_stride + vb);
@@ -519,18 +501,18 @@ __device__ __forceinline__ void issue_v(const Granules& gr, int32_t last, const 
     }
 }
 
-// The V operand of a tile from its ring stage. V load e (block vblk(e)) holds, in its quarter q
-// (256 bytes), the row of token 4*q + (e&3) of granule e>>2.
-//  * Transposed reads (one-byte formats at D = 256): for PV tile j (dims 16*j ..), 16-lane group
-//    qd needs its 8 tokens 4*qd + (r&3) of granule r>>2 (r = 0..7, the order P holds them) for
-//    every dim of the tile. ds_read_b64_tr_b8 takes, in each 16-lane group, an 8 x 16 byte
-//    block whose row r is the 8-byte pieces of lanes 2r and 2r+1, and gives lane n column n:
-//    so lane n points at row n/2 = block n/2, quarter qd, bytes 16*j + 8*(n&1). Slot j of the
-//    result holds dim 16*j + n of those tokens in k order (dwords 2*(j&1), 2*(j&1)+1 of v[j/2]).
+// The V operand of a tile from its ring stage.
+//  * Transposed reads (one-byte formats): for PV tile j (dims 16*j ..), 16-lane group qd needs
+//    its 8 tokens 4*qd + (r&3) of granule r>>2 (r = 0..7, the order P holds them) for every dim
+//    of the tile. ds_read_b64_tr_b8 takes, in each 16-lane group, an 8 x 16 byte block whose row
+//    r is the 8-byte pieces of lanes 2r and 2r+1, and gives lane n column n: so lane n points at
+//    row n/2's token, bytes 16*j + 8*(n&1) of it, and slot j of the result holds dim 16*j + n of
+//    the 8 tokens in k order (dwords 2*(j&1), 2*(j&1)+1 of v[j/2]). With 256-byte rows, V load e
+//    (block vblk(e)) holds in its quarter q the row of token 4*q + (e&3) of granule e>>2, so row
+//    r of group qd is block r, quarter qd; with 128-byte rows, token 4*qd + i of granule g is in
+//    load 2*g + (i&1), 128-byte row 2*qd + (i>>1) (Geo::vtok128).
 //  * 256-byte rows otherwise: slot e of lane (n, qd) is the 16 bytes of dims 16n.. of token
 //    4*qd + (e&3) of granule e>>2, stored by this very lane.
-//  * 128-byte rows: the 8 bytes of dims 8n.. (in v[e][0..1]), from where issue_v placed that
-//    token's row.
 template <class F>
 __device__ __forceinline__ TileV read_v(const uint8_t* stage, int n, int qd, int lane) {
     using G = Geo<F>;
@@ -538,25 +520,21 @@ __device__ __forceinline__ TileV read_v(const uint8_t* stage, int n, int qd, int
     const uint8_t* v0 = stage + G::VROW * 1024;
     if constexpr (F::VTR) {
         typedef int int2v __attribute__((ext_vector_type(2)));
-        const uint8_t* base = v0 + G::vblk(n >> 1) + 256 * qd + 8 * (n & 1);
+        const int r = n >> 1;
+        const uint8_t* base = F::ROW == 256
+                                  ? v0 + G::vblk(r) + 256 * qd + 8 * (n & 1)
+                                  : v0 + G::vblk(2 * (r >> 2) + (r & 1)) + 128 * (2 * qd + ((r >> 1) & 1)) + 8 * (n & 1);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < F::JT; ++j) {
             const int2v w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                 (__attribute__((address_space(3))) int2v*)(__attribute__((address_space(3))) const void*)(base + 16 * j));
             tv.v[j >> 1][2 * (j & 1)] = (uint32_t)w[0];
             tv.v[j >> 1][2 * (j & 1) + 1] = (uint32_t)w[1];
         }
-    } else if constexpr (F::ROW == 256) {
+    } else {
+        static_assert(F::ROW == 256, "128-byte rows take transposed reads");
 #pragma unroll
         for (int e = 0; e < 8; ++e) tv.v[e] = *reinterpret_cast<const u32x4*>(v0 + e * 1024 + 16 * lane);
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int t = 4 * qd + (e & 3);             // token within granule e >> 2
-            const uint8_t* a = v0 + (2 * (e >> 2) + (t >> 3)) * 1024 + 128 * G::vrow(t & 7) + 8 * n;
-            const uint2 w = *reinterpret_cast<const uint2*>(a);
-            tv.v[e] = u32x4{w.x, w.y, 0u, 0u};
-        }
     }
     return tv;
 }
@@ -883,14 +861,27 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>(
             issue_k<F>(gn, last, lo, stage, p, lane);
             float4v sacc[2][RT];
             F::template qk<RT>(tk, sacc, qop);
-            // V is read while the QK MFMAs run, so its LDS latency overlaps them and the softmax.
-            vm_wait_tile_v<F>();                // tile k's V has landed
-            const TileV tv = read_v<F>(stage_bytes, n, qd, lane);
-            lds_wait_all();
-            issue_v<F>(gn, last, lo, stage, p, n, qd, lane);
-            gn = granules<F>(j0 + (G::NS + 1) * kStride, last, pages, pg0, kbase, vbase, p);
+            // With 256-byte rows (one wave per SIMD) V is read while the QK MFMAs run, so its LDS
+            // latency overlaps them and the softmax; with 128-byte rows (two waves per SIMD, 256
+            // registers) after the softmax, where the other wave covers the latency and the
+            // scores no longer take registers.
+            TileV tv;
+            if constexpr (F::ROW == 256) {
+                vm_wait_tile_v<F>();            // tile k's V has landed
+                tv = read_v<F>(stage_bytes, n, qd, lane);
+                lds_wait_all();
+                issue_v<F>(gn, last, lo, stage, p, n, qd, lane);
+                gn = granules<F>(j0 + (G::NS + 1) * kStride, last, pages, pg0, kbase, vbase, p);
+            }
             typename F::PopT pop[RT];
             over = softmax_tile<RT, F::NG, F::TILE>(sacc, j0, mask_from, lim, c, m_ref, pop, qd);
+            if constexpr (F::ROW == 128) {
+                vm_wait_tile_v<F>();
+                tv = read_v<F>(stage_bytes, n, qd, lane);
+                lds_wait_all();
+                issue_v<F>(gn, last, lo, stage, p, n, qd, lane);
+                gn = granules<F>(j0 + (G::NS + 1) * kStride, last, pages, pg0, kbase, vbase, p);
+            }
             if (over) break;
             F::template pv<RT>(tv, pop, o);
             row_sums<RT>(pop, lsum);
