@@ -390,18 +390,22 @@ def main():
     env = verify_setup(torch, A, wl, w, dev)
     plan, lens, kv_bytes, token_heads, elem = env["plan"], env["lens"], env["kv_bytes"], env["token_heads"], env["elem"]
     c0 = env["cases"][0]
-    # split_kernel<format, row tiles, KV heads per workgroup>: format 0 = E4M3 D256, 1 = FP16 D128,
-    # 2 = E5M2 D256, 3 = FP16 D256, 4 = E4M3 D128; 16 packed rows per tile; a workgroup holds the
-    # largest group of KV heads (up to 4 for E4M3 D128, 2 otherwise) that divides Hkv while the
-    # grid still covers every CU (the library's rule).
+    # split_kernel<format, row tiles per wave, KV heads per workgroup, row groups>: format 0 = E4M3
+    # D256, 1 = FP16 D128, 2 = E5M2 D256, 3 = FP16 D256, 4 = E4M3 D128; 16 packed rows per tile; a
+    # workgroup holds the largest group of KV heads (up to 4 for E4M3 D128, 2 otherwise) that
+    # divides Hkv while the grid still covers every CU, and two row groups of half the row tiles
+    # each when a grid of one-head workgroups gives each CU at most one (formats other than E4M3
+    # D128, two or three row tiles) - the library's rules.
     fmt = {"e4m3": 0 if w.head_dim == 256 else 4, "fp16": 1 if w.head_dim == 128 else 3, "e5m2": 2}[w.kv_format]
     gs = plan.info["grid_splits"]
+    row_tiles = -(-plan.info["rows"] // 16)
     hp = 1
     for cand in ((4, 2) if fmt == 4 else (2,)):
         if w.num_kv_heads % cand == 0 and w.batch * (w.num_kv_heads // cand) * gs >= plan.info["num_cus"]:
             hp = cand
             break
-    kernel_name = f"split_kernel<{fmt}, {-(-plan.info['rows'] // 16)}, {hp}>"
+    rg = 2 if fmt != 4 and row_tiles >= 2 and hp == 1 and w.batch * w.num_kv_heads * gs <= plan.info["num_cus"] else 1
+    kernel_name = f"split_kernel<{fmt}, {-(-row_tiles // rg)}, {hp}, {rg}>"
 
     # The split kernel's own duration for the roofline: HIP events around every split launch on its
     # stream, taken once the launch time is steady (events add dispatch gaps, so they stay out of the

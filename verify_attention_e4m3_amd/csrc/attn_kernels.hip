@@ -11,10 +11,12 @@
 // "Scope" (FP16 operands, FP32 accumulation for QK and PV) and "Implementation and validation
 // in progress" (exact E4M3 -> FP16 conversion).
 //
-// Kernel design (two 64-lane waves per (slot, KV head, split); one or two KV heads per
-// workgroup):
+// Kernel design (two 64-lane waves per (slot, KV head, split); one, two or four KV heads per
+// workgroup, or, for grids of at most one workgroup per CU, one KV head with its rows split
+// over two wave pairs):
 //  * The packed rows (q_len verify tokens x G heads, up to 48) are the N dimension of every
-//    MFMA, so each K/V byte of a token range is read exactly once for all rows.
+//    MFMA, so each K/V byte of a token range is read exactly once for all rows (with two row
+//    groups, once per group, the second read mostly from L2).
 //  * S^T = K . Q^T on v_mfma_f32_16x16x32_f16: A = 16 tokens x 32 dims of K, B = 32 dims x 16
 //    rows of Q (Q stays in registers for the whole split). The dims are visited in a
 //    permuted order shared by A and B, chosen so each lane's K bytes are 4 contiguous 16-byte
@@ -276,9 +278,8 @@ template <> struct Fmt<kFmtF16D256> {
 
 // E4M3, D = 128: 128-byte token rows, 32-token tiles of two 16-token granules. K vector i
 // (i = 0, 1) of a lane holds dims 64*i + 16*qd + 0..15 and feeds k-steps 2i and 2i+1, as at
-// D = 256. For PV, lane (m, qd) needs dims 8m..8m+7 of its 8 tokens: each V slot holds the 16-byte
-// pair of dims 16*(m/2) + 0..15 (lanes m and m^1 load the same bytes, from the same cache
-// line), and the lane keeps its own half. MFMA j (0..7) covers dims 8m + j.
+// D = 256. PV tile j (0..7) covers dims 16*j .. 16*j + 15, its V^T operand from a transposed
+// LDS read (read_v).
 template <> struct Fmt<kFmtE4M3D128> {
     static constexpr int D = 128;
     static constexpr int KSTEPS = 4;
@@ -423,15 +424,22 @@ __device__ __forceinline__ Granules granules(int32_t j0, int32_t last, const int
 // Direct global -> LDS load of 16 bytes per lane from base + voff: lane l's bytes land at
 // lds + 16*l. Issued as inline asm so that the compiler's wait-count pass, which cannot tell
 // the two ring stages apart and would wait for every LDS load before any LDS read, leaves the
-// waiting to the explicit vmcnt waits of the tile loop. The KV cache is read exactly once, so
-// the loads carry the non-temporal (streaming) hint.
+// waiting to the explicit vmcnt waits of the tile loop. The KV cache is read once, so the loads
+// carry the non-temporal (streaming) hint (NT); with two row groups the same bytes are read by
+// two waves at about the same time, and plain loads let the second read hit in L2.
+template <bool NT>
 __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
     const uint64_t b64 = (uint64_t)base;
     const uint64_t sbase = join_words((uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32)),
                                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64));
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
-                 "v"(voff), "s"(sbase)
-                 : "memory", "m0");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
+                     "v"(voff), "s"(sbase)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
+                     "v"(voff), "s"(sbase)
+                     : "memory", "m0");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -447,15 +455,15 @@ constexpr int split_waves_per_simd() { return Fmt<FMT>::ROW == 128 ? 2 : 1; }
 // clamps each lane's token to `last` (whose page exists; the extra tokens are masked). A
 // prefetch past the split's end keeps the per-tile load count (so the ring's vmcnt accounting
 // is the same every iteration) but reads only token `last`'s row, which stays in L2.
-template <class F>
+template <class F, bool NT>
 __device__ __forceinline__ void issue_k(const Granules& gr, int32_t last, const LaneOffs& lo, uint32_t stage,
                                         const RunParams& p, int lane) {
     using G = Geo<F>;
     if (gr.j0 + F::TILE - 1 <= last && !gr.past_end) {
 #pragma unroll
         for (int i = 0; i < G::KL; ++i) {
-            dma16(gr.kA, lo.k[i], stage + i * 1024);
-            dma16(gr.kB, lo.k[i], stage + (G::KL + i) * 1024);
+            dma16<NT>(gr.kA, lo.k[i], stage + i * 1024);
+            dma16<NT>(gr.kB, lo.k[i], stage + (G::KL + i) * 1024);
         }
     } else {
         const int tr = lane / G::LPR, slot = lane % G::LPR;
@@ -467,13 +475,13 @@ __device__ __forceinline__ void issue_k(const Granules& gr, int32_t last, const 
             const uint32_t oa = (uint32_t)((min(gr.j0 + tok, last) - gr.j0) * p.k_token_stride) + sw;
             const uint32_t ob = (uint32_t)((min(gr.j0 + F::B_TOK + tok, last) - gr.gsB) * p.k_token_stride) + sw;
             const uint32_t oz = (uint32_t)((last - cap) * p.k_token_stride + 16 * slot);
-            dma16(gr.kA, gr.past_end ? oz : oa, stage + i * 1024);
-            dma16(gr.kB, gr.past_end ? oz : ob, stage + (G::KL + i) * 1024);
+            dma16<NT>(gr.kA, gr.past_end ? oz : oa, stage + i * 1024);
+            dma16<NT>(gr.kB, gr.past_end ? oz : ob, stage + (G::KL + i) * 1024);
         }
     }
 }
 
-template <class F>
+template <class F, bool NT>
 __device__ __forceinline__ void issue_v(const Granules& gr, int32_t last, const LaneOffs& lo, uint32_t stage,
                                         const RunParams& p, int n, int qd, int lane) {
     using G = Geo<F>;
@@ -482,8 +490,8 @@ __device__ __forceinline__ void issue_v(const Granules& gr, int32_t last, const 
     if (gr.j0 + F::TILE - 1 <= last && !gr.past_end) {
 #pragma unroll
         for (int e = 0; e < VPG; ++e) {
-            dma16(gr.vA, lo.v[e], v0 + G::vblk(e));
-            dma16(gr.vB, lo.v[e], v0 + G::vblk(VPG + e));
+            dma16<NT>(gr.vA, lo.v[e], v0 + G::vblk(e));
+            dma16<NT>(gr.vB, lo.v[e], v0 + G::vblk(VPG + e));
         }
     } else {
         // 256-byte rows: lane (n, qd) loads dims 16n.. of tokens 4qd + e; 128-byte rows: lane l
@@ -495,8 +503,8 @@ __device__ __forceinline__ void issue_v(const Granules& gr, int32_t last, const 
             const uint32_t oa = (uint32_t)((min(gr.j0 + rel, last) - gr.j0) * p.v_token_stride + vb);
             const uint32_t ob = (uint32_t)((min(gr.j0 + F::B_TOK + rel, last) - gr.gsB) * p.v_token_stride + vb);
             const uint32_t oz = (uint32_t)((last - gr.j0) * p.v_token_stride + vb);
-            dma16(gr.vA, gr.past_end ? oz : oa, v0 + G::vblk(e));
-            dma16(gr.vB, gr.past_end ? oz : ob, v0 + G::vblk(VPG + e));
+            dma16<NT>(gr.vA, gr.past_end ? oz : oa, v0 + G::vblk(e));
+            dma16<NT>(gr.vB, gr.past_end ? oz : ob, v0 + G::vblk(VPG + e));
         }
     }
 }
@@ -670,34 +678,47 @@ __device__ __forceinline__ void split_row_max(float (&m)[RT], int32_t j_begin, i
     }
 }
 
-// Split kernel: a workgroup holds HP KV heads of one (slot, split), two 64-lane waves per head;
-// RT row tiles of 16 packed rows. Wave w serves head HP*pair + w % HP and streams that head's
-// tiles w / HP, w / HP + 2, ... of the split through its own LDS ring; at the end the second
-// wave of each head hands its partial state to the first through LDS, which merges the two
-// (always its own first) and writes the head's split panel. Two waves per split halve the
-// number of splits, and with it the partial traffic, for the same number of waves in flight.
+// Split kernel: a workgroup holds HP KV heads of one (slot, split), two 64-lane waves per head
+// and row group, RT row tiles of 16 packed rows per wave. Wave w serves head HP*pair + w % HP and
+// streams that head's tiles (w / HP) % 2, (w / HP) % 2 + 2, ... of the split through its own LDS
+// ring; at the end the second wave of each pair hands its partial state to the first through
+// LDS, which merges the two (always its own first) and writes its rows of the split panel. Two
+// waves per split halve the number of splits, and with it the partial traffic, for the same
+// number of waves in flight.
 // With HP = 2 (even head counts) the waves of a workgroup read neighbouring head rows of the
 // same tokens, so one CU streams whole 2*D-byte runs of each token row instead of isolated
 // D-byte pieces; on MI355X that raises the sustained read rate of the paged stream by about a
 // tenth over one head per workgroup.
+// With RG = 2 row groups (HP = 1; grids that give each CU at most one workgroup, which would
+// otherwise leave half of its SIMDs idle) a second pair of waves takes row tiles RT .. 2*RT - 1
+// of the same head and tokens (past the head's last row tile, rows without a query: zero
+// scores, never written), so each wave's tile loop carries fewer rows and every SIMD works.
+// Each row's tiles, references, products and merge are the same in both layouts, and a pair
+// recomputes with exact row maxima exactly when one of the two pairs' waves of the same token
+// half exceeded a reference - the same tokens and rows whose overflow decides the recompute of
+// a one-group wave - so the row groups never change a bit of the result.
 constexpr int kWavesPerHead = 2;
 
-template <int HP, int RING>
+template <int NW, int RING>
 struct SplitLds {
-    __attribute__((aligned(16))) uint8_t rings[kWavesPerHead * HP][RING];
+    __attribute__((aligned(16))) uint8_t rings[NW][RING];
     int32_t pages[kMaxSplitPages];
+    int32_t over[NW];
 };
 
-template <int FMT, int RT, int HP>
-__global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>()) void split_kernel(RunParams p) {
+template <int FMT, int RT, int HP, int RG>
+__global__ __launch_bounds__(64 * kWavesPerHead * HP * RG, split_waves_per_simd<FMT>()) void split_kernel(RunParams p) {
+    static_assert(RG == 1 || (RG == 2 && HP == 1), "row groups split one head's rows");
     using F = Fmt<FMT>;
     constexpr int D = F::D;
     constexpr int KS = F::KSTEPS;
     constexpr int JT = F::JT;
+    constexpr int NW = kWavesPerHead * HP * RG;                  // waves per workgroup
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform within a wave
-    const int hl = wave % HP;      // head within the workgroup
-    const int half = wave / HP;    // which of the head's two waves
+    const int hl = wave % HP;                      // head within the workgroup
+    const int half = (wave / HP) % kWavesPerHead;  // which of the pair's two waves
+    const int rt0 = (wave / (HP * kWavesPerHead)) * RT;   // the wave's first row tile
     const int n = lane & 15;       // MFMA column = packed row within a row tile
     const int qd = lane >> 4;      // quarter of the wave
 
@@ -738,13 +759,13 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>(
     const int32_t last = j_end - 1;
 
     // Q^T operands stay in registers for the whole split: entry (rt, ks) holds the 8 dims of
-    // k-step ks (F::q_dim) of packed row rt*16 + n (zeros past q_len*G) - the dim order of the
-    // K operand, so the contraction pairs matching dims.
+    // k-step ks (F::q_dim) of packed row (rt0 + rt)*16 + n (zeros past q_len*G) - the dim order of
+    // the K operand, so the contraction pairs matching dims.
     half8 qop[RT][KS];
     int32_t lim[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        const int r = rt * 16 + n;
+        const int r = (rt0 + rt) * 16 + n;
         const int t = r / p.group;
         const int h = g * p.group + (r - t * p.group);
         const bool live = r < p.rows;
@@ -784,14 +805,14 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>(
     // LDS: the waves' rings, then the split's block-table entries (shared by the workgroup's
     // heads), clamped into the caches and staged once: the tile loop then issues no
     // compiler-visible global load (whose wait would also drain the ring).
-    __shared__ SplitLds<HP, Geo<F>::RING> lds;
+    __shared__ SplitLds<NW, Geo<F>::RING> lds;
     int32_t* pages = lds.pages;
     int32_t pg0, pg_last, unused_slot;
     locate(j_begin, p, pg0, unused_slot);
     locate(last, p, pg_last, unused_slot);
     {
         const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
-        for (int i = threadIdx.x; i <= pg_last - pg0; i += 64 * kWavesPerHead * HP) {
+        for (int i = threadIdx.x; i <= pg_last - pg0; i += 64 * NW) {
             const int32_t v = bt[pg0 + i];
             pages[i] = v < 0 ? 0 : (v >= p.num_pages ? (int32_t)(p.num_pages - 1) : v);
         }
@@ -821,9 +842,9 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>(
     // which the wave sees a key for it; exponentials are taken against it, so O and l never
     // need rescaling and the O accumulators are touched only by MFMAs. A later tile may exceed
     // the reference by up to kRefSlack (P <= 2^kRefSlack, exact range in FP16 and FP32). If one
-    // exceeds it by more, the wave recomputes its tiles once with each row's exact maximum
-    // over the split as its reference (then no tile can exceed it). Both passes depend only on
-    // the split's own data, so the result is deterministic.
+    // exceeds it by more, the wave (with row groups: both waves of its token half) recomputes its
+    // tiles once with each row's exact maximum over the split as its reference (then no tile can
+    // exceed it). Both passes depend only on the split's own data, so the result is deterministic.
     float m_ref[RT];
     float4v lsum[RT];        // row sums of P: every element of lane (n, qd) holds packed row n's
     float4v o[RT][JT];
@@ -839,8 +860,8 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>(
 #pragma unroll
         for (int k = 0; k < G::NS; ++k) {
             const Granules gk = granules<F>(first + k * kStride, last, pages, pg0, kbase, vbase, p);
-            issue_k<F>(gk, last, lo, ring0 + k * G::STAGE, p, lane);
-            issue_v<F>(gk, last, lo, ring0 + k * G::STAGE, p, n, qd, lane);
+            issue_k<F, RG == 1>(gk, last, lo, ring0 + k * G::STAGE, p, lane);
+            issue_v<F, RG == 1>(gk, last, lo, ring0 + k * G::STAGE, p, n, qd, lane);
         }
         bool over = false;
         int32_t j0 = first;
@@ -858,7 +879,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>(
                 for (int i = 0; i < G::CH; ++i)
                     tk.k[tt][i] = *reinterpret_cast<const u32x4*>(stage_bytes + tt * G::KL * 1024 + k_rd[i]);
             lds_wait_all();
-            issue_k<F>(gn, last, lo, stage, p, lane);
+            issue_k<F, RG == 1>(gn, last, lo, stage, p, lane);
             float4v sacc[2][RT];
             F::template qk<RT>(tk, sacc, qop);
             // With 256-byte rows (one wave per SIMD) V is read while the QK MFMAs run, so its LDS
@@ -870,7 +891,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>(
                 vm_wait_tile_v<F>();            // tile k's V has landed
                 tv = read_v<F>(stage_bytes, n, qd, lane);
                 lds_wait_all();
-                issue_v<F>(gn, last, lo, stage, p, n, qd, lane);
+                issue_v<F, RG == 1>(gn, last, lo, stage, p, n, qd, lane);
                 gn = granules<F>(j0 + (G::NS + 1) * kStride, last, pages, pg0, kbase, vbase, p);
             }
             typename F::PopT pop[RT];
@@ -879,7 +900,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>(
                 vm_wait_tile_v<F>();
                 tv = read_v<F>(stage_bytes, n, qd, lane);
                 lds_wait_all();
-                issue_v<F>(gn, last, lo, stage, p, n, qd, lane);
+                issue_v<F, RG == 1>(gn, last, lo, stage, p, n, qd, lane);
                 gn = granules<F>(j0 + (G::NS + 1) * kStride, last, pages, pg0, kbase, vbase, p);
             }
             if (over) break;
@@ -894,19 +915,37 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>(
 
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) m_ref[rt] = -INFINITY;
-    if (run_pass()) {
-        split_row_max<FMT, RT>(m_ref, j_begin, j_end, mask_from, lim, c, pages, pg0, kbase, vbase, p, qop, n, qd);
-        run_pass();
+    bool over = run_pass();
+    if constexpr (RG == 1) {
+        if (over) {
+            split_row_max<FMT, RT>(m_ref, j_begin, j_end, mask_from, lim, c, pages, pg0, kbase, vbase, p, qop, n, qd);
+            run_pass();
+        }
+    } else {
+        // The other row group's wave of the same token half (wave ^ 2) covers the rest of the
+        // rows over the same tiles: a wave recomputes if either exceeded a reference. The flags
+        // are read as wave-uniform values, so every branch here is a scalar one, and the second
+        // barrier (the recompute reuses the rings) is taken by every wave or by none.
+        if (lane == 0) lds.over[wave] = over ? 1 : 0;
+        __syncthreads();
+        const bool any = __builtin_amdgcn_readfirstlane(lds.over[0] | lds.over[1] | lds.over[2] | lds.over[3]) != 0;
+        if (any) {
+            if (__builtin_amdgcn_readfirstlane(lds.over[wave] | lds.over[wave ^ 2]) != 0) {
+                split_row_max<FMT, RT>(m_ref, j_begin, j_end, mask_from, lim, c, pages, pg0, kbase, vbase, p, qop, n, qd);
+                run_pass();
+            }
+            __syncthreads();
+        }
     }
 
-    // Hand-over: each head's second wave writes its accumulators (element i of O^T tile (rt, j)
+    // Hand-over: each pair's second wave writes its accumulators (element i of O^T tile (rt, j)
     // as row (rt*JT + j)*4 + i of 64 lanes), its references and its row sums into the
-    // head's region of the rings; the first wave reads the same lane's values back, so both
+    // pair's region of the rings; the first wave reads the same lane's values back, so both
     // sides are conflict-free.
     constexpr int kXferFloats = (RT * JT * 4 + 2 * RT) * 64;
-    static_assert(HP * kXferFloats * 4 <= sizeof(lds.rings), "hand-over must fit in the rings");
+    static_assert(HP * RG * kXferFloats * 4 <= sizeof(lds.rings), "hand-over must fit in the rings");
     __syncthreads();                         // every wave is done with its ring
-    float* xfer = reinterpret_cast<float*>(&lds.rings[0][0]) + hl * kXferFloats;
+    float* xfer = reinterpret_cast<float*>(&lds.rings[0][0]) + (hl + (rt0 / RT) * HP) * kXferFloats;
     if (half == 1) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -924,17 +963,18 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP, split_waves_per_simd<FMT>(
     // Merge (first wave, then second) and write the head's split panel: O^T tile j holds
     // O[row n][dim F::o_dim(qd, i, j)] in element i; the four elements of a tile (transposed V
     // reads) or, for a fixed i, groups of 4 consecutive j (otherwise) are 4 consecutive dims.
-    const int rows_alloc = 16 * RT;
+    const int rows_alloc = RG == 1 ? 16 * RT : p.rows_alloc;
     float* panel = p.ws + ((int64_t)(b * p.num_kv_heads + g) * p.grid_splits + s) * p.split_floats;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
+        if (RG == 2 && 16 * (rt0 + rt) >= rows_alloc) break;     // past the head's last row tile
         const float m1 = xfer[(RT * JT * 4 + rt) * 64 + lane];
         const float l1 = xfer[(RT * JT * 4 + RT + rt) * 64 + lane];
         const float m0 = m_ref[rt];
         const float M = fmaxf(m0, m1);
         const float a0 = m0 == -INFINITY ? 0.0f : fast_exp2(m0 - M);
         const float a1 = m1 == -INFINITY ? 0.0f : fast_exp2(m1 - M);
-        const int r = rt * 16 + n;
+        const int r = (rt0 + rt) * 16 + n;
         float* orow = panel + r * D;
         if constexpr (F::VTR) {
             // the four elements of a tile are four consecutive dims
@@ -1045,9 +1085,9 @@ typedef void (*KernelFn)(RunParams);
 template <int FMT, int HP>
 KernelFn split_for_rows(int row_tiles) {
     switch (row_tiles) {
-        case 1: return split_kernel<FMT, 1, HP>;
-        case 2: return split_kernel<FMT, 2, HP>;
-        default: return split_kernel<FMT, 3, HP>;
+        case 1: return split_kernel<FMT, 1, HP, 1>;
+        case 2: return split_kernel<FMT, 2, HP, 1>;
+        default: return split_kernel<FMT, 3, HP, 1>;
     }
 }
 
@@ -1063,10 +1103,23 @@ inline int heads_per_workgroup(int num_kv_heads, int batch, int grid_splits, int
     return 1;
 }
 
+// Row groups per head: two (a second pair of waves on the second half of the row tiles) for
+// one-wave-per-SIMD formats with two or three row tiles when even the full grid of one-head
+// workgroups gives each CU at most one, so that its four waves use all of the CU's SIMDs;
+// otherwise one. The result does not depend on the choice.
+inline int row_groups(bool one_wave_per_simd, int row_tiles, int hp, int batch, int num_kv_heads, int grid_splits,
+                      int num_cus) {
+    const bool small = (int64_t)batch * num_kv_heads * grid_splits <= num_cus;
+    return one_wave_per_simd && row_tiles >= 2 && hp == 1 && small ? 2 : 1;
+}
+
 template <int FMT>
-KernelFn split_for(int row_tiles, int hp) {
+KernelFn split_for(int row_tiles, int hp, int rg) {
     if constexpr (Fmt<FMT>::ROW == 128) {
         if (hp == 4) return split_for_rows<FMT, 4>(row_tiles);
+    } else {
+        // two groups of ceil(row_tiles / 2) row tiles
+        if (rg == 2) return row_tiles == 2 ? split_kernel<FMT, 1, 1, 2> : split_kernel<FMT, 2, 1, 2>;
     }
     return hp == 2 ? split_for_rows<FMT, 2>(row_tiles) : split_for_rows<FMT, 1>(row_tiles);
 }
@@ -1080,19 +1133,20 @@ attn_status attn_launch_split(const attn_plan_s* plan, const attn::RunParams& p,
     const int row_tiles = p.rows_alloc / 16;
     const bool rows128 = plan->desc.kv_dtype == ATTN_KV_E4M3 && plan->desc.head_dim == 128;
     const int hp = attn::heads_per_workgroup(p.num_kv_heads, p.batch, p.grid_splits, plan->num_cus, rows128 ? 4 : 2);
+    const int rg = attn::row_groups(!rows128, row_tiles, hp, p.batch, p.num_kv_heads, p.grid_splits, plan->num_cus);
     attn::KernelFn fn;
     if (rows128)
-        fn = attn::split_for<attn::kFmtE4M3D128>(row_tiles, hp);
+        fn = attn::split_for<attn::kFmtE4M3D128>(row_tiles, hp, 1);
     else if (plan->desc.kv_dtype == ATTN_KV_FP16)
-        fn = plan->desc.head_dim == 256 ? attn::split_for<attn::kFmtF16D256>(row_tiles, hp)
-                                        : attn::split_for<attn::kFmtF16D128>(row_tiles, hp);
+        fn = plan->desc.head_dim == 256 ? attn::split_for<attn::kFmtF16D256>(row_tiles, hp, rg)
+                                        : attn::split_for<attn::kFmtF16D128>(row_tiles, hp, rg);
     else if (plan->desc.kv_dtype == ATTN_KV_E5M2)
-        fn = attn::split_for<attn::kFmtE5M2D256>(row_tiles, hp);
+        fn = attn::split_for<attn::kFmtE5M2D256>(row_tiles, hp, rg);
     else
-        fn = attn::split_for<attn::kFmtE4M3D256>(row_tiles, hp);
+        fn = attn::split_for<attn::kFmtE4M3D256>(row_tiles, hp, rg);
     // One workgroup per (slot, split, group of hp KV heads); the kernel decodes the same order.
     const unsigned grid = (unsigned)p.batch * (p.num_kv_heads / hp) * p.grid_splits;
-    hipError_t e = hipLaunchKernel((const void*)fn, dim3(grid), dim3(64 * attn::kWavesPerHead * hp), kargs, 0,
+    hipError_t e = hipLaunchKernel((const void*)fn, dim3(grid), dim3(64 * attn::kWavesPerHead * hp * rg), kargs, 0,
                                    (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
