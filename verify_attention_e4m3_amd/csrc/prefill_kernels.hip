@@ -209,17 +209,35 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
         };
         auto qk = [&](int32_t blk, float4v (&sacc)[2][RT]) {
             const uint8_t* kst = stage_k(blk);
+            // K operands are read PD k-steps ahead of their MFMAs (a fence keeps the reads there;
+            // left alone, the scheduler moves each read next to its use): 1-2% faster than one
+            // step ahead.
+            constexpr int PD = 4;
+            auto kread = [&](int ks, int gr) {
+                const int row = 16 * gr + n;
+                const int chunk = (4 * ks + qd) ^ (row & 15);
+                return *reinterpret_cast<const half8*>(kst + row * kPfRowBytes + chunk * 16);
+            };
+            half8 ka[PD + 1][2];
+#pragma unroll
+            for (int ks = 0; ks < PD; ++ks)
+#pragma unroll
+                for (int gr = 0; gr < 2; ++gr) ka[ks][gr] = kread(ks, gr);
 #pragma unroll
             for (int gr = 0; gr < 2; ++gr)
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) sacc[gr][rt] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
+                if (ks + PD < 8) {
+#pragma unroll
+                    for (int gr = 0; gr < 2; ++gr) ka[(ks + PD) % (PD + 1)][gr] = kread(ks + PD, gr);
+                }
+                // keep the reads ahead of this k-step's MFMAs (VALU and SALU may still move)
+                __builtin_amdgcn_sched_barrier(0x406);
 #pragma unroll
                 for (int gr = 0; gr < 2; ++gr) {
-                    const int row = 16 * gr + n;
-                    const int chunk = (4 * ks + qd) ^ (row & 15);
-                    const half8 a = *reinterpret_cast<const half8*>(kst + row * kPfRowBytes + chunk * 16);
+                    const half8 a = ka[ks % (PD + 1)][gr];
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt)
                         sacc[gr][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qop[rt][ks], sacc[gr][rt], 0, 0, 0);
