@@ -494,23 +494,27 @@ def test_reference_slack_overflow_recompute(batch, fmt, head_dim, row_tiles):
     compare(run_gpu(c, plan), run_oracle(c))
 
 
-@pytest.mark.parametrize("fmt,head_dim", [("e4m3", 256), ("e5m2", 256), ("fp16", 256), ("fp16", 128)])
-def test_row_group_workgroups_recompute_like_batched_bitwise(fmt, head_dim):
+_ROW_GROUP_CASES = [("e4m3", 256, 8), ("e5m2", 256, 8), ("fp16", 256, 8), ("fp16", 128, 8), ("e4m3", 256, 4)]
+
+
+@pytest.mark.parametrize("fmt,head_dim,q_len", _ROW_GROUP_CASES,
+                         ids=[f"{f}-d{d}-q{q}" for f, d, q in _ROW_GROUP_CASES])
+def test_row_group_workgroups_recompute_like_batched_bitwise(fmt, head_dim, q_len):
     # One slot alone gives a grid of at most one workgroup per CU, which the library runs with two
-    # row groups per KV head (a second pair of waves on the last row tiles); B8 of the same 65536-
-    # token plan runs one group. Spiked keys past the first 64 tokens of every 512-token split
-    # score only the rows of the last row tile (packed rows 32..47, Q = 1) more than the slack
-    # above their reference; the other rows (Q scaled by 0.05) stay within it, but their bits
-    # still depend on whether their wave recomputes. Both layouts must recompute the same rows:
-    # each slot alone gives the batched bits, and both match the oracle.
+    # row groups per KV head (a second pair of waves on the last row tiles: tiles 2..3 of 48 rows
+    # at q8, tile 1 of 24 rows at q4); B8 of the same 65536-token plan runs one group. Spiked keys
+    # past the first 64 tokens of every 512-token split score only the rows of the second group
+    # (Q = 1) more than the slack above their reference; the other rows (Q scaled by 0.05) stay
+    # within it, but their bits still depend on whether their wave recomputes. Both layouts must
+    # recompute the same rows: each slot alone gives the batched bits, and both match the oracle.
     lens = [900, 700, 1000, 513, 64, 899, 640, 1023]
-    note(f"row groups vs one group under a partial recompute, {fmt} D{head_dim}")
-    c = _case(batch=8, seq_lens=lens, q_len=8, num_q_heads=24, num_kv_heads=4, head_dim=head_dim,
-              page_size=16, seed=61 + head_dim, kv_format=fmt, max_seq_len=65536)
+    note(f"row groups vs one group under a partial recompute, {fmt} D{head_dim} q{q_len}")
+    c = _case(batch=8, seq_lens=lens, q_len=q_len, num_q_heads=24, num_kv_heads=4, head_dim=head_dim,
+              page_size=16, seed=61 + head_dim + q_len, kv_format=fmt, max_seq_len=65536)
     G = 6
-    rows = torch.arange(8 * G, device="cuda")
-    hot = (rows >= 32).view(8, G)                               # [t][j]: packed row t*G + j
-    q = c["q"].view(8, 8, 4, G, head_dim)                       # [b][t][g][j][d]
+    rows = torch.arange(q_len * G, device="cuda")
+    hot = (rows >= (32 if q_len == 8 else 16)).view(q_len, G)   # [t][j]: packed row t*G + j
+    q = c["q"].view(8, q_len, 4, G, head_dim)                   # [b][t][g][j][d]
     q.mul_(torch.where(hot, 1.0, 0.05).to(q.dtype)[None, :, None, :, None])
     q.masked_fill_(hot[None, :, None, :, None], 1.0)
     kc = c["k_cache"]

@@ -637,6 +637,13 @@ __device__ __forceinline__ void row_sums(const half4 (&pop)[RT], float4v (&lsum)
     for (int rt = 0; rt < RT; ++rt) lsum[rt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pop[rt], lsum[rt], 0, 0, 0);
 }
 
+// a0*x0 + a1*x1 with the rounding spelled out (the first product rounded, the second fused), so
+// that every instantiation of the split kernel - whatever its row tiles, heads or row groups -
+// merges a row's two halves to the same bits (left to the compiler, the contraction may differ).
+__device__ __forceinline__ float merge2(float a0, float x0, float a1, float x1) {
+    return __builtin_fmaf(a1, x1, a0 * x0);
+}
+
 // Exact maximum of every row's scaled, masked scores over the split (log2 units; -inf for a
 // row that sees no key in it). Used only by the rare recompute of a split; plain global loads.
 template <int FMT, int RT>
@@ -982,7 +989,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP * RG, split_waves_per_simd<
             for (int j = 0; j < JT; ++j) {
                 float4v v;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = a0 * o[rt][j][i] + a1 * xfer[((rt * JT + j) * 4 + i) * 64 + lane];
+                for (int i = 0; i < 4; ++i) v[i] = merge2(a0, o[rt][j][i], a1, xfer[((rt * JT + j) * 4 + i) * 64 + lane]);
                 *reinterpret_cast<float4v*>(orow + F::o_dim(qd, 0, j)) = v;
             }
         } else {
@@ -994,12 +1001,12 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP * RG, split_waves_per_simd<
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int j = 4 * c4 + u;
-                        v[u] = a0 * o[rt][j][i] + a1 * xfer[((rt * JT + j) * 4 + i) * 64 + lane];
+                        v[u] = merge2(a0, o[rt][j][i], a1, xfer[((rt * JT + j) * 4 + i) * 64 + lane]);
                     }
                     *reinterpret_cast<float4v*>(orow + F::o_dim(qd, i, 4 * c4)) = v;
                 }
         }
-        const float l = a0 * lsum[rt][0] + a1 * l1;
+        const float l = merge2(a0, lsum[rt][0], a1, l1);
         if (qd == 0) {
             panel[rows_alloc * D + r] = M;
             panel[rows_alloc * D + rows_alloc + r] = l;
@@ -1068,8 +1075,12 @@ __global__ __launch_bounds__(256) void combine_kernel(RunParams p) {
                     ov[u] = *reinterpret_cast<const floatv*>(orow + (int64_t)min(s0 + u, s_last) * p.split_floats);
             }
 #pragma unroll
-            for (int u = 0; u < kChunk; ++u)      // lane s0+u < 64 holds split s0+u's weight (0 past S)
-                acc += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), s0 + u)) * ov[u];
+            for (int u = 0; u < kChunk; ++u) {    // lane s0+u < 64 holds split s0+u's weight (0 past S)
+                const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), s0 + u));
+                // fused multiply-add spelled out, so every dim split (DS) rounds the sum the same way
+#pragma unroll
+                for (int i = 0; i < VW; ++i) acc[i] = __builtin_fmaf(wu, ov[u][i], acc[i]);
+            }
         }
     }
     const float scale = den > 0.0f ? (*p.v_scale) / den : 0.0f;
