@@ -320,6 +320,38 @@ def test_slot_permutation_permutes_the_output_bitwise():
     compare(base, oracle_pairs(c, [(4, 0), (1, 3), (2, 1)]))
 
 
+_LAYOUT_CASES = [
+    # (q_len, Hq, Hkv, format, D): one row tile at q1 (the D128 FP16 decode shape) and q2, two
+    # row tiles at q3 (one slot alone: two row groups of one tile each)
+    (1, 32, 8, "fp16", 128),
+    (2, 24, 4, "e5m2", 256),
+    (3, 24, 4, "e4m3", 256),
+    (3, 24, 4, "fp16", 256),
+]
+
+
+@pytest.mark.parametrize("q_len,hq,hkv,fmt,head_dim", _LAYOUT_CASES,
+                         ids=[f"q{q}-H{a}/{b}-{f}-d{d}" for q, a, b, f, d in _LAYOUT_CASES])
+def test_workgroup_layouts_equal_single_bitwise(q_len, hq, hkv, fmt, head_dim):
+    # B8 of a 65536-token plan fills the chip (head-pair workgroups, one row group); each slot
+    # alone runs one-head workgroups (with two row groups where it has two row tiles). Every
+    # layout computes a row the same way, so each slot alone gives the batched bits.
+    lens = [3297, 0, 40000, 8, 131, 65536, 1, 20000]
+    note(f"layouts vs single, q{q_len} Hq{hq}/Hkv{hkv} {fmt} D{head_dim}")
+    c = _case(batch=8, seq_lens=lens, q_len=q_len, num_q_heads=hq, num_kv_heads=hkv, head_dim=head_dim,
+              page_size=1648, seed=71 + q_len + hkv, kv_format=fmt, max_seq_len=65536)
+    plan = plan_for(c)
+    gs, cus = plan.info["grid_splits"], plan.info["num_cus"]
+    assert 8 * (hkv // 2) * gs >= cus > hkv * gs        # batched pairs heads; one slot is a small grid
+    batched = run_gpu(c, plan)
+    short = [0, 3, 4, 6]                                 # the oracle on the short rows
+    compare(batched[short], run_oracle({**c, **{k: c[k][short] for k in ("q", "block_table", "seq_lens")}}))
+    for b in range(8):
+        one = {k: (v[b:b + 1] if k in ("q", "block_table", "seq_lens") else v) for k, v in c.items()}
+        single = run_gpu(one, batch_capacity=1)
+        assert torch.equal(single[0].view(torch.int16), batched[b].view(torch.int16)), b
+
+
 def test_paired_head_workgroups_equal_single_bitwise():
     # B8 at Hkv4 and 64K fills the chip with workgroups that hold two KV heads each; one slot
     # alone runs one head per workgroup. Both run each head's split the same way.
