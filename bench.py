@@ -395,7 +395,8 @@ def main():
     # workgroup holds the largest group of KV heads (up to 4 for E4M3 D128, 2 otherwise) that
     # divides Hkv while the grid still covers every CU, and two row groups of half the row tiles
     # each when a grid of one-head workgroups gives each CU at most one (formats other than E4M3
-    # D128, two or three row tiles) - the library's rules.
+    # D128, two or three row tiles; three groups of one row tile for the one-byte D256 formats at
+    # three row tiles) - the library's rules.
     fmt = {"e4m3": 0 if w.head_dim == 256 else 4, "fp16": 1 if w.head_dim == 128 else 3, "e5m2": 2}[w.kv_format]
     gs = plan.info["grid_splits"]
     row_tiles = -(-plan.info["rows"] // 16)
@@ -406,6 +407,8 @@ def main():
             break
     rg = 2 if fmt != 4 and row_tiles >= 2 and hp == 1 and w.batch * w.num_kv_heads * gs <= plan.info["num_cus"] else 1
     kernel_name = f"split_kernel<{fmt}, {-(-row_tiles // rg)}, {hp}, {rg}>"
+    if rg == 2 and row_tiles == 3 and fmt in (0, 2):
+        kernel_name = f"split_kernel_rg3<{fmt}>"           # three row groups, one row tile per wave
 
     # The split kernel's own duration for the roofline: HIP events around every split launch on its
     # stream, taken once the launch time is steady (events add dispatch gaps, so they stay out of the

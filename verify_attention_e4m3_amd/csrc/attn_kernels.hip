@@ -13,10 +13,10 @@
 //
 // Kernel design (two 64-lane waves per (slot, KV head, split); one, two or four KV heads per
 // workgroup, or, for grids of at most one workgroup per CU, one KV head with its rows split
-// over two wave pairs):
+// over two or three wave pairs):
 //  * The packed rows (q_len verify tokens x G heads, up to 48) are the N dimension of every
 //    MFMA, so each K/V byte of a token range is read exactly once for all rows (with two row
-//    groups, once per group, the second read mostly from L2).
+//    groups, once per group, the second read mostly from L2; with three, into one shared ring).
 //  * S^T = K . Q^T on v_mfma_f32_16x16x32_f16: A = 16 tokens x 32 dims of K, B = 32 dims x 16
 //    rows of Q (Q stays in registers for the whole split). The dims are visited in a
 //    permuted order shared by A and B, chosen so each lane's K bytes are 4 contiguous 16-byte
@@ -1014,6 +1014,268 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP * RG, split_waves_per_simd<
     }
 }
 
+// The softmax step without the exit (for loops that every wave of a workgroup must run to the
+// same end): a row whose tile max exceeds its reference by more than the slack sets `over` (per
+// lane) and P is computed against the unchanged references - that pass's result is discarded
+// and recomputed. Without an overflow it computes exactly what softmax_tile computes.
+template <int RT, int NG, int TILE, class PopT>
+__device__ __forceinline__ void softmax_tile_nx(const float4v (&sacc)[2][RT], int32_t j0, int32_t mask_from,
+                                                const int32_t (&lim)[RT], float c, float (&m_ref)[RT],
+                                                PopT (&pop)[RT], int qd, bool& over) {
+    constexpr int NV = 4 * NG;
+    float x[RT][NV];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int tt = 0; tt < NG; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[rt][tt * 4 + i] = sacc[tt][rt][i];
+    if (j0 + TILE > mask_from) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int tt = 0; tt < NG; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    x[rt][tt * 4 + i] = (j0 + 16 * tt + 4 * qd + i) < lim[rt] ? x[rt][tt * 4 + i] : -INFINITY;
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        float m = NG == 2 ? max3f(max3f(x[rt][0], x[rt][1], x[rt][2]), max3f(x[rt][3], x[rt][4 % NV], x[rt][5 % NV]),
+                                  max3f(x[rt][6 % NV], x[rt][7 % NV], x[rt][7 % NV]))
+                          : max3f(max3f(x[rt][0], x[rt][1], x[rt][2]), x[rt][3], x[rt][3]);
+        m = quad_max(m);
+        m *= c;
+        over |= m > m_ref[rt] + kRefSlack && m_ref[rt] != -INFINITY;
+        if (m_ref[rt] == -INFINITY) m_ref[rt] = m;
+        const float neg_m = m_ref[rt] == -INFINITY ? 0.0f : -m_ref[rt];
+#pragma unroll
+        for (int e = 0; e < NV; ++e) pop[rt][e] = (_Float16)fast_exp2(__builtin_fmaf(x[rt][e], c, neg_m));
+    }
+}
+
+// Three row groups (one-byte formats at D = 256, 33 to 48 packed rows, grids of at most one
+// workgroup per CU): six waves per (slot, KV head, split), wave w taking row tile w / 2 over the
+// tiles of token half w % 2. The three waves of a half share one three-stage LDS ring: the
+// second of them (row tile 1; waves 2 and 3, the two waves alone on their SIMDs - waves 4 and 5
+// share SIMDs with waves 0 and 1) issues the K and V loads of each tile, and one barrier per
+// tile both publishes tile k (the loader has waited for its own loads) and frees the stage of
+// tile k-1 (every wave has read it), which then takes tile k+2. Per wave this is a third of the rows' MFMA
+// and softmax work of the one-group kernel, and six waves keep every SIMD busy. Every wave runs
+// the same number of iterations (the shorter half idles through its last one) and the loop has
+// no exit; a half recomputes with exact row maxima when any of its three waves saw a tile exceed
+// a reference by more than the slack - the rows and tiles whose overflow decides the recompute of
+// the one-group wave of that half - so the result has the same bits as the other layouts.
+constexpr int kRg3Waves = 6;
+constexpr int kRg3Stages = 3;
+
+template <int FMT>
+__global__ __launch_bounds__(64 * kRg3Waves) void split_kernel_rg3(RunParams p) {
+    using F = Fmt<FMT>;
+    using G = Geo<F>;
+    static_assert(F::ROW == 256 && F::VTR && F::NG == 2, "one-byte formats at D = 256");
+    constexpr int D = F::D;
+    constexpr int KS = F::KSTEPS;
+    constexpr int JT = F::JT;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform within a wave
+    const int half = wave & 1;                 // token half: tiles half, half + 2, ...
+    const int rg = wave >> 1;                  // row tile
+    const int n = lane & 15;
+    const int qd = lane >> 4;
+
+    // Workgroup order as in split_kernel (one KV head per workgroup).
+    int wg = blockIdx.x;
+    const int g = wg % p.num_kv_heads;
+    wg /= p.num_kv_heads;
+    const int s = wg % p.grid_splits;
+    int b = wg / p.grid_splits;
+    int32_t L;
+    if (p.order_by_work) {
+        const int32_t Ll = lane < p.batch ? clamp_len(p.seq_lens[lane], p.max_seq_len) : 0;
+        const int32_t wk = lane < p.batch ? (Ll > 0 ? partition_len(Ll, p.policy) : 0) : -1;
+        int rank = 0;
+        for (int k = 0; k < p.batch; ++k) {
+            const int32_t wkk = __builtin_amdgcn_readlane(wk, k);
+            rank += (wkk > wk) | ((wkk == wk) & (k < lane));
+        }
+        const uint64_t hit = __ballot(lane < p.batch && rank == b);
+        if (hit != 0) b = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+        L = __builtin_amdgcn_readlane(Ll, b);
+    } else {
+        L = clamp_len(p.seq_lens[b], p.max_seq_len);
+    }
+    const int32_t S = num_splits(L, p.policy);
+    if (s >= S) return;                 // uniform over the workgroup
+    const int32_t P = partition_len(L, p.policy);
+    const int32_t j_begin = s * P;
+    const int32_t j_end = min(j_begin + P, L);
+    const int32_t last = j_end - 1;
+
+    // Q^T operands and visibility limit of this wave's row tile (as in split_kernel).
+    half8 qop[1][KS];
+    int32_t lim[1];
+    {
+        const int r = rg * 16 + n;
+        const int t = r / p.group;
+        const int h = g * p.group + (r - t * p.group);
+        const bool live = r < p.rows;
+        const uint16_t* qrow = p.q + (((int64_t)b * p.q_len + (live ? t : 0)) * p.num_q_heads + (live ? h : 0)) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const half8 v = *reinterpret_cast<const half8*>(qrow + F::q_dim(ks, qd));
+            qop[0][ks] = live ? v : half8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+        const int32_t lr = p.causal ? (L - p.q_len + 1 + t) : L;
+        lim[0] = min(lr, j_end);
+    }
+    float c = p.sm_scale * (*p.k_scale) * kLog2e;
+    if (c < 0.0f) {
+        c = -c;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qop[0][ks] = -qop[0][ks];
+    }
+    c = fmaxf(c, 1.17549435e-38f);
+#pragma unroll
+    for (int ks = 0; ks < KS; ks += 2) asm volatile("" ::"v"(qop[0][ks]), "v"(qop[0][ks + 1]));
+    const int32_t mask_from = p.causal ? min(j_end, L - p.q_len + 1) : j_end;
+
+    const uint8_t* kbase = p.k + (int64_t)g * p.k_head_stride;
+    const uint8_t* vbase = p.v + (int64_t)g * p.v_head_stride;
+    struct Rg3Lds {
+        __attribute__((aligned(16))) uint8_t rings[2][kRg3Stages * G::STAGE];
+        int32_t pages[kMaxSplitPages];
+        int32_t over[kRg3Waves];
+    };
+    __shared__ Rg3Lds lds;
+    int32_t* pages = lds.pages;
+    int32_t pg0, pg_last, unused_slot;
+    locate(j_begin, p, pg0, unused_slot);
+    locate(last, p, pg_last, unused_slot);
+    {
+        const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
+        for (int i = threadIdx.x; i <= pg_last - pg0; i += 64 * kRg3Waves) {
+            const int32_t v = bt[pg0 + i];
+            pages[i] = v < 0 ? 0 : (v >= p.num_pages ? (int32_t)(p.num_pages - 1) : v);
+        }
+    }
+    __syncthreads();
+
+    uint8_t* ring = lds.rings[half];
+    const uint32_t ring0 = lds_addr(ring);
+    const LaneOffs lo = lane_offsets<F>(p, lane, n, qd);
+    uint32_t k_rd[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) k_rd[i] = n * F::ROW + 16 * ((4 * i + qd) ^ G::swz(n));
+    constexpr int32_t kStride = 2 * F::TILE;
+    const int32_t first = j_begin + half * F::TILE;
+    const int32_t ntiles = (j_end - j_begin + F::TILE - 1) / F::TILE;
+    const int iters = (ntiles + 1) >> 1;               // the first half's tile count, uniform
+
+    float m_ref[1];
+    float4v lsum[1];
+    float4v o[1][JT];
+    // The loads of the half's tile t, issued by row group 1 (past the split's end: re-reads of the
+    // last row, as in split_kernel).
+    auto load_tile = [&](int32_t t, int stage) {
+        const Granules gr = granules<F>(first + t * kStride, last, pages, pg0, kbase, vbase, p);
+        if (rg == 1) {
+            issue_k<F, true>(gr, last, lo, ring0 + stage * G::STAGE, p, lane);
+            issue_v<F, true>(gr, last, lo, ring0 + stage * G::STAGE, p, n, qd, lane);
+        }
+    };
+    // One pass over the split; every wave runs `iters` iterations with one barrier each. With
+    // `compute` false the wave only keeps the ring going (its half needs no recompute).
+    auto run_pass = [&](bool compute) -> bool {
+        bool over = false;
+        if (compute) {
+            lsum[0] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < JT; ++j) o[0][j] = float4v{0.f, 0.f, 0.f, 0.f};
+        }
+        load_tile(0, 0);
+        load_tile(1, 1);
+        int32_t j0 = first;
+        for (int it = 0; it < iters; ++it) {
+            // The loader's loads of tile `it` have landed (tile it+1's may still be in flight).
+            if (rg == 1) vm_wait_n<G::KLOADS + G::VLOADS>();
+            __syncthreads();                   // tile it in LDS for all; tile it-1 read by all
+            load_tile(it + 2, (it + 2) % kRg3Stages);
+            if (compute && j0 <= last) {
+                const uint8_t* stage_bytes = ring + (it % kRg3Stages) * G::STAGE;
+                TileK tk;
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int i = 0; i < G::CH; ++i)
+                        tk.k[tt][i] = *reinterpret_cast<const u32x4*>(stage_bytes + tt * G::KL * 1024 + k_rd[i]);
+                float4v sacc[2][1];
+                F::template qk<1>(tk, sacc, qop);
+                const TileV tv = read_v<F>(stage_bytes, n, qd, lane);
+                typename F::PopT pop[1];
+                softmax_tile_nx<1, F::NG, F::TILE>(sacc, j0, mask_from, lim, c, m_ref, pop, qd, over);
+                F::template pv<1>(tv, pop, o);
+                row_sums<1>(pop, lsum);
+                lds_wait_all();                // this tile's reads are done before the next barrier
+            }
+            j0 += kStride;
+        }
+        vm_wait_all();
+        return __any(over);
+    };
+
+    m_ref[0] = -INFINITY;
+    const bool over1 = run_pass(true);
+    if (lane == 0) lds.over[wave] = over1 ? 1 : 0;
+    __syncthreads();
+    const bool any = __builtin_amdgcn_readfirstlane(lds.over[0] | lds.over[1] | lds.over[2] | lds.over[3] |
+                                                     lds.over[4] | lds.over[5]) != 0;
+    if (any) {
+        // a half recomputes when any of its three waves overflowed; the other half keeps its pass
+        const bool redo = __builtin_amdgcn_readfirstlane(lds.over[half] | lds.over[half + 2] | lds.over[half + 4]) != 0;
+        if (redo) split_row_max<FMT, 1>(m_ref, j_begin, j_end, mask_from, lim, c, pages, pg0, kbase, vbase, p, qop, n, qd);
+        run_pass(redo);
+    }
+
+    // Hand-over per row tile (second half to first) and panel rows, as in split_kernel.
+    constexpr int kXferFloats = (JT * 4 + 2) * 64;
+    static_assert(3 * kXferFloats * 4 <= sizeof(lds.rings), "hand-over must fit in the rings");
+    __syncthreads();                         // every wave is done with the rings
+    float* xfer = reinterpret_cast<float*>(&lds.rings[0][0]) + rg * kXferFloats;
+    if (half == 1) {
+#pragma unroll
+        for (int j = 0; j < JT; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xfer[(j * 4 + i) * 64 + lane] = o[0][j][i];
+        xfer[(JT * 4) * 64 + lane] = m_ref[0];
+        xfer[(JT * 4 + 1) * 64 + lane] = lsum[0][0];
+    }
+    __syncthreads();
+    if (half == 1) return;
+    constexpr int rows_alloc = 48;
+    float* panel = p.ws + ((int64_t)(b * p.num_kv_heads + g) * p.grid_splits + s) * p.split_floats;
+    const float m1 = xfer[(JT * 4) * 64 + lane];
+    const float l1 = xfer[(JT * 4 + 1) * 64 + lane];
+    const float m0 = m_ref[0];
+    const float M = fmaxf(m0, m1);
+    const float a0 = m0 == -INFINITY ? 0.0f : fast_exp2(m0 - M);
+    const float a1 = m1 == -INFINITY ? 0.0f : fast_exp2(m1 - M);
+    const int r = rg * 16 + n;
+    float* orow = panel + r * D;
+#pragma unroll
+    for (int j = 0; j < JT; ++j) {
+        float4v v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = merge2(a0, o[0][j][i], a1, xfer[(j * 4 + i) * 64 + lane]);
+        *reinterpret_cast<float4v*>(orow + F::o_dim(qd, 0, j)) = v;
+    }
+    const float l = merge2(a0, lsum[0][0], a1, l1);
+    if (qd == 0) {
+        panel[rows_alloc * D + r] = M;
+        panel[rows_alloc * D + rows_alloc + r] = l;
+    }
+}
+
 // Log-sum-exp combine: one wave per packed row. Lane s loads split s's (m, l) while every lane
 // already loads its D/64 dims of the first 16 splits' O, so the row costs about one memory
 // round trip; the max and the denominator are wave reductions in a fixed tree, each split's
@@ -1155,10 +1417,17 @@ attn_status attn_launch_split(const attn_plan_s* plan, const attn::RunParams& p,
         fn = attn::split_for<attn::kFmtE5M2D256>(row_tiles, hp, rg);
     else
         fn = attn::split_for<attn::kFmtE4M3D256>(row_tiles, hp, rg);
+    // Three row groups for the one-byte D256 formats at three row tiles (one row tile per wave).
+    int waves = attn::kWavesPerHead * hp * rg;
+    if (rg == 2 && row_tiles == 3 && plan->desc.head_dim == 256 &&
+        (plan->desc.kv_dtype == ATTN_KV_E4M3 || plan->desc.kv_dtype == ATTN_KV_E5M2)) {
+        fn = plan->desc.kv_dtype == ATTN_KV_E4M3 ? attn::split_kernel_rg3<attn::kFmtE4M3D256>
+                                                 : attn::split_kernel_rg3<attn::kFmtE5M2D256>;
+        waves = attn::kRg3Waves;
+    }
     // One workgroup per (slot, split, group of hp KV heads); the kernel decodes the same order.
     const unsigned grid = (unsigned)p.batch * (p.num_kv_heads / hp) * p.grid_splits;
-    hipError_t e = hipLaunchKernel((const void*)fn, dim3(grid), dim3(64 * attn::kWavesPerHead * hp * rg), kargs, 0,
-                                   (hipStream_t)stream);
+    hipError_t e = hipLaunchKernel((const void*)fn, dim3(grid), dim3(64 * waves), kargs, 0, (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
