@@ -526,26 +526,29 @@ def test_reference_slack_overflow_recompute(batch, fmt, head_dim, row_tiles):
     compare(run_gpu(c, plan), run_oracle(c))
 
 
-_ROW_GROUP_CASES = [("e4m3", 256, 8), ("e5m2", 256, 8), ("fp16", 256, 8), ("fp16", 128, 8), ("e4m3", 256, 4)]
+_ROW_GROUP_CASES = [("e4m3", 256, 8, 32), ("e5m2", 256, 8, 32), ("fp16", 256, 8, 32), ("fp16", 128, 8, 32),
+                    ("e4m3", 256, 4, 16), ("e4m3", 256, 8, 16), ("e5m2", 256, 8, 0)]
 
 
-@pytest.mark.parametrize("fmt,head_dim,q_len", _ROW_GROUP_CASES,
-                         ids=[f"{f}-d{d}-q{q}" for f, d, q in _ROW_GROUP_CASES])
-def test_row_group_workgroups_recompute_like_batched_bitwise(fmt, head_dim, q_len):
-    # One slot alone gives a grid of at most one workgroup per CU, which the library runs with two
-    # row groups per KV head (a second pair of waves on the last row tiles: tiles 2..3 of 48 rows
-    # at q8, tile 1 of 24 rows at q4); B8 of the same 65536-token plan runs one group. Spiked keys
-    # past the first 64 tokens of every 512-token split score only the rows of the second group
-    # (Q = 1) more than the slack above their reference; the other rows (Q scaled by 0.05) stay
-    # within it, but their bits still depend on whether their wave recomputes. Both layouts must
-    # recompute the same rows: each slot alone gives the batched bits, and both match the oracle.
+@pytest.mark.parametrize("fmt,head_dim,q_len,hot_tile", _ROW_GROUP_CASES,
+                         ids=[f"{f}-d{d}-q{q}-hot{h}" for f, d, q, h in _ROW_GROUP_CASES])
+def test_row_group_workgroups_recompute_like_batched_bitwise(fmt, head_dim, q_len, hot_tile):
+    # One slot alone gives a grid of at most one workgroup per CU, which the library runs with row
+    # groups per KV head: two (a second pair of waves on the last row tiles: tiles 2..3 of 48 rows
+    # at q8, tile 1 of 24 rows at q4) or, for the one-byte formats at D256 and 48 rows, three (one
+    # row tile per wave pair); B8 of the same 65536-token plan runs one group. Spiked keys past the
+    # first 64 tokens of every 512-token split score only the rows of the 16-row tile starting at
+    # `hot_tile` (Q = 1) more than the slack above their reference; the other rows (Q scaled by
+    # 0.05) stay within it, but their bits still depend on whether their wave recomputes. Both
+    # layouts must recompute the same rows: each slot alone gives the batched bits, and both match
+    # the oracle.
     lens = [900, 700, 1000, 513, 64, 899, 640, 1023]
     note(f"row groups vs one group under a partial recompute, {fmt} D{head_dim} q{q_len}")
     c = _case(batch=8, seq_lens=lens, q_len=q_len, num_q_heads=24, num_kv_heads=4, head_dim=head_dim,
               page_size=16, seed=61 + head_dim + q_len, kv_format=fmt, max_seq_len=65536)
     G = 6
     rows = torch.arange(q_len * G, device="cuda")
-    hot = (rows >= (32 if q_len == 8 else 16)).view(q_len, G)   # [t][j]: packed row t*G + j
+    hot = ((rows >= hot_tile) & (rows < hot_tile + 16)).view(q_len, G)   # [t][j]: packed row t*G + j
     q = c["q"].view(8, q_len, 4, G, head_dim)                   # [b][t][g][j][d]
     q.mul_(torch.where(hot, 1.0, 0.05).to(q.dtype)[None, :, None, :, None])
     q.masked_fill_(hot[None, :, None, :, None], 1.0)
@@ -558,7 +561,7 @@ def test_row_group_workgroups_recompute_like_batched_bitwise(fmt, head_dim, q_le
             kc[pages, j % ps] = _ONE[fmt]
     plan = plan_for(c)
     gs, cus = plan.info["grid_splits"], plan.info["num_cus"]
-    assert 8 * 4 * gs > cus >= 4 * gs          # batched: one group; one slot: two row groups
+    assert 8 * 4 * gs > cus >= 4 * gs          # batched: one group; one slot: row groups
     batched = run_gpu(c, plan)
     compare(batched, run_oracle(c))
     for b in range(8):
