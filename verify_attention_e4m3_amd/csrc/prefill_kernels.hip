@@ -6,7 +6,7 @@
 // token t sees keys j <= kv_len - q_len + t (every key when not causal). The long prefill of
 // "SM70 attention and quantized projection coverage across TP sizes" (sections "Scope" and
 // "Accumulation audit and rejected tuning": a Q8192 chunk against a 262144-token context,
-// D = 256, six query heads per KV head, FP16 inputs, FP32 accumulation for both QK and PV, a
+// D = 256, six query heads per KV head, FP16 operands with both products summed in FP32, a
 // full-width prefix plus a causal triangular tail).
 //
 // Kernel design (an MFMA-bound dense contraction, unlike the HBM-bound verify kernel):

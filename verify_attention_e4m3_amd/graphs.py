@@ -7,8 +7,8 @@ single-request optimization was missing from concurrent decode":
 
 * graphs are captured for a set of verify batch sizes, all bounded by one served context
   window (at most 262144 tokens);
-* before a bounded graph is used, every live request's CPU length hint is checked against that
-  window: a single oversized peer sends the whole batch to the ordinary (eager) route;
+* a bounded graph is replayed only when the host-side length hint of each live request fits
+  that window: a single oversized peer sends the whole batch to the ordinary (eager) route;
 * a live batch smaller than the graph is padded with zero-length slots, which the kernels never
   read (their queries and block-table rows may hold anything);
 * capture runs from the largest batch size down, so the workspace bank allocates the largest
