@@ -26,10 +26,11 @@
 //    from registers (the PV contraction visits keys in the order S^T holds them). The PV A
 //    operand (16 dims x 8 keys per lane group) comes straight from the row-major V block through
 //    gfx950's transposed LDS read (ds_read_b64_tr_b16), two reads per dim tile.
-//  * Softmax in log2 units against a fixed per-row reference (the maximum of the first block in
-//    which the row sees a key), so the O accumulators are only ever touched by MFMAs. A later
-//    block may exceed the reference by up to 2^10 (exact range in FP16 and FP32); if any row of
-//    the workgroup exceeds it by more, the workgroup recomputes with each row's exact maximum
+//  * Softmax in log2 units against a fixed per-row reference (the maximum of block 0, the first
+//    block of every row that sees a key), so the O accumulators are only ever touched by MFMAs
+//    and later blocks need no row maximum at all: the loop only keeps the largest exponential.
+//    A later score may exceed the reference by up to 2^10 (exact range in FP16 and FP32); if any
+//    exponential of the workgroup exceeds 2^10, it recomputes with each row's exact maximum
 //    from a QK-only pass. Both passes depend only on the data, so results are deterministic.
 //  * Q (3 row tiles x 256 dims) stays in registers for the whole key loop; O^T (3 x 256 x 16
 //    FP32 per wave) lives in accumulation registers.
@@ -58,7 +59,7 @@ constexpr int kPfD = 256;
 constexpr int kPfRowBytes = kPfD * 2;                        // one token row of one head
 constexpr int kPfStageBytes = kPfBlock * kPfRowBytes;        // 16 KB: one K (or V) block
 constexpr int kPfLoadsPerWave = kPfStageBytes / 1024 / kPfWaves;   // 4 K + 4 V per wave and block
-constexpr float kPfSlack = 10.0f;                            // log2 headroom over the reference
+constexpr float kPfSlackFactor = 1024.0f;                    // 2^10: headroom over the reference
 
 // Max over lanes l, l^16, l^32, l^48 (one MFMA column's four quarter-wave partials) with the
 // gfx950 lane swaps (v_permlane32_swap: l <-> l^32, v_permlane16_swap: l <-> l^16), VALU only.
@@ -95,13 +96,41 @@ struct PrefillLds {
 // 2i + l/32, slot l%32, and fetches that row's 16-byte chunk (l%32) ^ (row%16) for K and
 // (l%32) ^ 2*(row%16) for V (V is read in 32-byte pieces, so its swizzle moves whole pairs of
 // chunks). Rows past the sequence re-read its last token (they are masked).
+// Per-lane byte offsets of a full block's loads (row 2i + l/32 of the block and its chunk), fixed
+// for the kernel.
+struct PfLoadOffs {
+    uint32_t k[kPfLoadsPerWave];
+    uint32_t v[kPfLoadsPerWave];
+};
+
+__device__ __forceinline__ PfLoadOffs pf_load_offsets(const PrefillParams& p, int wave, int lane) {
+    PfLoadOffs lo;
+    const int slot = lane & 31;
+#pragma unroll
+    for (int u = 0; u < kPfLoadsPerWave; ++u) {
+        const int row = 2 * (wave * kPfLoadsPerWave + u) + (lane >> 5);
+        lo.k[u] = (uint32_t)(row * p.k_token_stride * 2) + (uint32_t)(slot ^ (row & 15)) * 16;
+        lo.v[u] = (uint32_t)(row * p.v_token_stride * 2) + (uint32_t)(slot ^ (2 * (row & 15))) * 16;
+    }
+    return lo;
+}
+
 __device__ __forceinline__ void pf_issue_block(const PrefillParams& p, const uint8_t* kbase, const uint8_t* vbase,
                                                int32_t blk, uint32_t k_stage, uint32_t v_stage, int wave,
-                                               int lane) {
+                                               int lane, const PfLoadOffs& lo) {
     const int32_t key0 = blk * kPfBlock;
-    const int32_t last = p.kv_len - 1 - key0;                // last valid row of this block
     const uint8_t* kb = kbase + (int64_t)key0 * p.k_token_stride * 2;
     const uint8_t* vb = vbase + (int64_t)key0 * p.v_token_stride * 2;
+    if (key0 + kPfBlock <= p.kv_len) {                       // a full block: the fixed offsets
+#pragma unroll
+        for (int u = 0; u < kPfLoadsPerWave; ++u) {
+            const int i = wave * kPfLoadsPerWave + u;
+            pf_dma16(kb, lo.k[u], k_stage + i * 1024);
+            pf_dma16(vb, lo.v[u], v_stage + i * 1024);
+        }
+        return;
+    }
+    const int32_t last = p.kv_len - 1 - key0;                // last valid row of this block
     const int slot = lane & 31;
 #pragma unroll
     for (int u = 0; u < kPfLoadsPerWave; ++u) {
@@ -178,140 +207,133 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
 
     float4v o[RT][16];
     float m_ref[RT], l_run[RT];
+    const PfLoadOffs lo = pf_load_offsets(p, wave, lane);
 
-    // Up to three passes over the key blocks, one loop body: pass 0 accumulates against each
-    // row's fixed reference (set on its first visible block). If some row of the workgroup
-    // exceeded its reference by more than the slack, pass 1 computes only S and takes each
-    // row's exact scaled maximum as its reference, and pass 2 accumulates again from zero
-    // (it cannot exceed those maxima).
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        m_ref[rt] = -INFINITY;
-        l_run[rt] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) o[rt][j] = float4v{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int pass_no = 0; pass_no < 3; ++pass_no) {
-        const bool max_only = pass_no == 1;                    // workgroup-uniform
-        // The key loop has no early exit and always updates O (a pass whose result is dropped
-        // still runs to its end): a loop exit that skips the O update keeps the compiler from
-        // accumulating in place.
-        bool over = false;
-        // Software pipeline over the blocks: iteration b computes S of block b+1 (its MFMAs are
-        // independent of, and so overlap, the softmax VALU work of block b), then the softmax and
-        // PV of block b. Block i lives in ring stage i % 4; at iteration b the ring holds K of
-        // b+1, V of b, block b+2 in flight and the stage of b+3 being loaded.
-        auto stage_k = [&](int32_t blk) { return &lds.k[blk % kPfStages][0]; };
-        auto stage_v = [&](int32_t blk) { return &lds.v[blk % kPfStages][0]; };
-        auto issue = [&](int32_t blk) {
-            const int sn = blk % kPfStages;
-            pf_issue_block(p, kbase, vbase, blk, k0 + sn * kPfStageBytes, v0 + sn * kPfStageBytes, wave, lane);
+    auto stage_k = [&](int32_t blk) { return &lds.k[blk % kPfStages][0]; };
+    auto issue = [&](int32_t blk) {
+        const int sn = blk % kPfStages;
+        pf_issue_block(p, kbase, vbase, blk, k0 + sn * kPfStageBytes, v0 + sn * kPfStageBytes, wave, lane, lo);
+    };
+    auto qk = [&](int32_t blk, float4v (&sacc)[2][RT]) {
+        const uint8_t* kst = stage_k(blk);
+        // K operands are read PD k-steps ahead of their MFMAs (a fence keeps the reads there;
+        // left alone, the scheduler moves each read next to its use): 1-2% faster than one
+        // step ahead.
+        constexpr int PD = 4;
+        auto kread = [&](int ks, int gr) {
+            const int row = 16 * gr + n;
+            const int chunk = (4 * ks + qd) ^ (row & 15);
+            return *reinterpret_cast<const half8*>(kst + row * kPfRowBytes + chunk * 16);
         };
-        auto qk = [&](int32_t blk, float4v (&sacc)[2][RT]) {
-            const uint8_t* kst = stage_k(blk);
-            // K operands are read PD k-steps ahead of their MFMAs (a fence keeps the reads there;
-            // left alone, the scheduler moves each read next to its use): 1-2% faster than one
-            // step ahead.
-            constexpr int PD = 4;
-            auto kread = [&](int ks, int gr) {
-                const int row = 16 * gr + n;
-                const int chunk = (4 * ks + qd) ^ (row & 15);
-                return *reinterpret_cast<const half8*>(kst + row * kPfRowBytes + chunk * 16);
-            };
-            half8 ka[PD + 1][2];
+        half8 ka[PD + 1][2];
 #pragma unroll
-            for (int ks = 0; ks < PD; ++ks)
+        for (int ks = 0; ks < PD; ++ks)
 #pragma unroll
-                for (int gr = 0; gr < 2; ++gr) ka[ks][gr] = kread(ks, gr);
+            for (int gr = 0; gr < 2; ++gr) ka[ks][gr] = kread(ks, gr);
+#pragma unroll
+        for (int gr = 0; gr < 2; ++gr)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) sacc[gr][rt] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            if (ks + PD < 8) {
+#pragma unroll
+                for (int gr = 0; gr < 2; ++gr) ka[(ks + PD) % (PD + 1)][gr] = kread(ks + PD, gr);
+            }
+            // keep the reads ahead of this k-step's MFMAs (VALU and SALU may still move)
+            __builtin_amdgcn_sched_barrier(0x406);
+#pragma unroll
+            for (int gr = 0; gr < 2; ++gr) {
+                const half8 a = ka[ks % (PD + 1)][gr];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    sacc[gr][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qop[rt][ks], sacc[gr][rt], 0, 0, 0);
+            }
+        }
+    };
+    // Row maximum of a block's scores (masked keys excluded), scaled to log2 units; lane (n, qd)
+    // holds keys key0 + 16*gr + 4*qd + i of its row, the other three quarters the rest.
+    auto row_max = [&](int32_t blk, const float4v (&sacc)[2][RT], int rt, bool masked) {
+        const int32_t key0 = blk * kPfBlock;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int gr = 0; gr < 2; ++gr)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x = sacc[gr][rt][i];
+                mx = fmaxf(mx, (!masked || (key0 + 16 * gr + 4 * qd + i) < lim[rt]) ? x : -INFINITY);
+            }
+        return pf_quad_max(mx) * c;
+    };
+    // Exponentials against the fixed references, row sums, and P for the PV product. `emax`
+    // keeps the largest exponential: one above 2^slack means some score exceeded its reference
+    // by more than the slack.
+    float emax = 0.0f;
+    auto softmax = [&](int32_t blk, const float4v (&sacc)[2][RT], half8 (&pop)[RT], auto masked_tag) {
+        constexpr bool kMasked = decltype(masked_tag)::value;
+        const int32_t key0 = blk * kPfBlock;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const float neg = -m_ref[rt];
+            float e[8];
 #pragma unroll
             for (int gr = 0; gr < 2; ++gr)
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt) sacc[gr][rt] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                if (ks + PD < 8) {
-#pragma unroll
-                    for (int gr = 0; gr < 2; ++gr) ka[(ks + PD) % (PD + 1)][gr] = kread(ks + PD, gr);
+                for (int i = 0; i < 4; ++i) {
+                    float v = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[gr][rt][i], c, neg));
+                    // a row without a visible key has reference -inf and only masked blocks
+                    if constexpr (kMasked) v = (key0 + 16 * gr + 4 * qd + i) < lim[rt] ? v : 0.0f;
+                    e[4 * gr + i] = v;
                 }
-                // keep the reads ahead of this k-step's MFMAs (VALU and SALU may still move)
-                __builtin_amdgcn_sched_barrier(0x406);
 #pragma unroll
-                for (int gr = 0; gr < 2; ++gr) {
-                    const half8 a = ka[ks % (PD + 1)][gr];
+            for (int k = 0; k < 8; ++k) l_run[rt] += e[k];
+            emax = fmaxf(fmaxf(emax, fmaxf(e[0], e[1])), fmaxf(fmaxf(e[2], e[3]), fmaxf(e[4], e[5])));
+            emax = fmaxf(emax, fmaxf(e[6], e[7]));
 #pragma unroll
-                    for (int rt = 0; rt < RT; ++rt)
-                        sacc[gr][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qop[rt][ks], sacc[gr][rt], 0, 0, 0);
-                }
-            }
-        };
-        auto soft_pv = [&](int32_t blk, float4v (&sacc)[2][RT], auto masked_tag) {
-            constexpr bool kMasked = decltype(masked_tag)::value;
-            const int32_t key0 = blk * kPfBlock;
-            // Lane (n, qd) holds keys key0 + 16*gr + 4*qd + i of its row.
-            half8 pop[RT];
+            for (int k = 0; k < 8; ++k) pop[rt][k] = (_Float16)e[k];
+        }
+    };
+    auto pv = [&](int32_t blk, const half8 (&pop)[RT]) {
+        // O^T += V^T . P^T over the block's keys in the order 4*qd + e (e < 4) of granule 0,
+        // then 16 + 4*qd + e - 4 (e >= 4), as P holds them. The V^T operand of dim tile jd
+        // (dims 16*jd + 0..15) comes from two transposed LDS reads (ds_read_b64_tr_b16): in
+        // each 16-lane group, lane n points at 4 dims (16*jd + 4*(n%4) ..) of key base + n/4,
+        // and lane n receives dim 16*jd + n of the group's 4 keys. Group qd reads keys 4*qd..
+        // (base 0) and 16 + 4*qd.. (base 16, 8 KB further in the stage).
+        const uint8_t* vst = &lds.v[blk % kPfStages][0];
+        const int vrow = 4 * qd + (n >> 2);                  // < 16: row % 16 of both reads
+        const uint32_t vlane = (uint32_t)(vrow * kPfRowBytes + 8 * (n & 3));
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                float mx = -INFINITY;
+        for (int jd = 0; jd < 16; ++jd) {
+            const uint8_t* a0 = vst + vlane + (uint32_t)(32 * (jd ^ vrow));
+            const short4v lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) short4v*)(__attribute__((address_space(3))) const void*)a0);
+            const short4v hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) short4v*)(__attribute__((address_space(3))) const void*)(
+                    a0 + 16 * kPfRowBytes));
+            const half8 ah = __builtin_bit_cast(half8, short8v{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]});
 #pragma unroll
-                for (int gr = 0; gr < 2; ++gr)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float x = sacc[gr][rt][i];
-                        if constexpr (kMasked) x = (key0 + 16 * gr + 4 * qd + i) < lim[rt] ? x : -INFINITY;
-                        sacc[gr][rt][i] = x;
-                        mx = fmaxf(mx, x);
-                    }
-                mx = pf_quad_max(mx);
-                const float ms = mx * c;
-                // Branch-free, so that the whole iteration is one scheduling region: the max pass
-                // keeps the running maximum, the others set a row's reference on its first
-                // visible block and flag any block that exceeds it by more than the slack.
-                const float first = m_ref[rt] == -INFINITY ? ms : m_ref[rt];
-                m_ref[rt] = max_only ? fmaxf(m_ref[rt], ms) : first;
-                over |= !max_only && ms > m_ref[rt] + kPfSlack;
-#pragma unroll
-                for (int gr = 0; gr < 2; ++gr)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float x = sacc[gr][rt][i];
-                        // unmasked blocks hold finite scores only, and every row has a reference
-                        const float e = (kMasked && x == -INFINITY)
-                                            ? 0.0f
-                                            : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -m_ref[rt]));
-                        l_run[rt] += e;
-                        pop[rt][4 * gr + i] = (_Float16)e;
-                    }
-            }
-            // O^T += V^T . P^T over the block's keys in the order 4*qd + e (e < 4) of granule 0,
-            // then 16 + 4*qd + e - 4 (e >= 4), as P holds them. The V^T operand of dim tile jd
-            // (dims 16*jd + 0..15) comes from two transposed LDS reads (ds_read_b64_tr_b16): in
-            // each 16-lane group, lane n points at 4 dims (16*jd + 4*(n%4) ..) of key base + n/4,
-            // and lane n receives dim 16*jd + n of the group's 4 keys. Group qd reads keys 4*qd..
-            // (base 0) and 16 + 4*qd.. (base 16, 8 KB further in the stage).
-            const uint8_t* vst = stage_v(blk);
-            const int vrow = 4 * qd + (n >> 2);                  // < 16: row % 16 of both reads
-            const uint32_t vlane = (uint32_t)(vrow * kPfRowBytes + 8 * (n & 3));
-#pragma unroll
-            for (int jd = 0; jd < 16; ++jd) {
-                const uint8_t* a0 = vst + vlane + (uint32_t)(32 * (jd ^ vrow));
-                const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) short4v*)(__attribute__((address_space(3))) const void*)a0);
-                const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) short4v*)(__attribute__((address_space(3))) const void*)(
-                        a0 + 16 * kPfRowBytes));
-                const half8 ah = __builtin_bit_cast(half8, short8v{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
-                    o[rt][jd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, pop[rt], o[rt][jd], 0, 0, 0);
-            }
-        };
+            for (int rt = 0; rt < RT; ++rt)
+                o[rt][jd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, pop[rt], o[rt][jd], 0, 0, 0);
+        }
+    };
 
+    // Blocks that end at or below every row's visible limit need no mask; the rest (the causal
+    // tail and the ragged end of the keys) run the masked copy of the loop body.
+    const int32_t nfull = min(nblk, mask_from / kPfBlock);
+    // One pass over the key blocks, software-pipelined: iteration b computes S of block b+1 (its
+    // MFMAs are independent of, and so overlap, the VALU work on block b), then consumes block b
+    // (`consume(b, S, masked)`). Block i lives in ring stage i % 4; at iteration b the ring holds
+    // K of b+1, V of b, block b+2 in flight and the stage of b+3 being loaded. `first(S)` sees
+    // block 0's scores before the loop.
+    auto run_pass = [&](auto consume, auto first) {
         float4v s_cur[2][RT];
         for (int32_t i = 0; i < min(nblk, kPfStages - 1); ++i) issue(i);
         if (nblk > 0) {
             pf_wait_loads(min(nblk, kPfStages - 1) - 1);      // block 0 of this wave has landed
             __syncthreads();
             qk(0, s_cur);
+            first(s_cur);
         }
         auto iteration = [&](int32_t b, auto masked_tag) {
             // Block b+1 (if any) has landed everywhere, and iteration b-1 is done everywhere, so
@@ -321,31 +343,56 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
             if (b + kPfStages - 1 < nblk) issue(b + kPfStages - 1);
             float4v s_next[2][RT];
             qk(b + 1 < nblk ? b + 1 : b, s_next);             // past the end: a discarded re-read
-            soft_pv(b, s_cur, masked_tag);
+            consume(b, s_cur, masked_tag);
 #pragma unroll
             for (int gr = 0; gr < 2; ++gr)
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) s_cur[gr][rt] = s_next[gr][rt];
         };
-        // Blocks that end at or below every row's visible limit need no mask; the rest (the causal
-        // tail and the ragged end of the keys) run the masked copy of the softmax.
-        const int32_t nfull = min(nblk, mask_from / kPfBlock);
         for (int32_t b = 0; b < nfull; ++b) iteration(b, std::false_type{});
         for (int32_t b = nfull; b < nblk; ++b) iteration(b, std::true_type{});
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // no load may still write the ring
-        const bool redo = __syncthreads_or(over) != 0;          // also frees the ring for a next pass
-        if (pass_no == 0 && !redo) break;                       // the common case: one pass
-        if (pass_no == 1) {
+    };
+    auto accumulate = [&](int32_t b, const float4v (&sacc)[2][RT], auto masked_tag) {
+        half8 pop[RT];
+        softmax(b, sacc, pop, masked_tag);
+        pv(b, pop);
+    };
+    auto clear = [&]() {
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                l_run[rt] = 0.0f;
+        for (int rt = 0; rt < RT; ++rt) {
+            l_run[rt] = 0.0f;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) o[rt][j] = float4v{0.f, 0.f, 0.f, 0.f};
-            }
-        } else if (pass_no == 0) {
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) m_ref[rt] = -INFINITY;
+            for (int j = 0; j < 16; ++j) o[rt][j] = float4v{0.f, 0.f, 0.f, 0.f};
         }
+    };
+
+    // The first pass: each row's reference is the maximum of block 0 (every row that sees a key
+    // sees key 0, so this is its first visible block; a row that sees none keeps -inf and only
+    // has masked blocks).
+    clear();
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) m_ref[rt] = -INFINITY;
+    run_pass(accumulate, [&](const float4v (&s0)[2][RT]) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) m_ref[rt] = row_max(0, s0, rt, nfull == 0);
+    });
+    // Some score above its reference by more than the slack, anywhere in the workgroup: a QK-only
+    // pass takes each row's exact maximum as its reference, and the accumulation runs again (it
+    // cannot exceed those maxima). The barrier also frees the ring for a next pass.
+    if (__syncthreads_or(emax > kPfSlackFactor) != 0) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) m_ref[rt] = -INFINITY;
+        run_pass(
+            [&](int32_t b, const float4v (&sacc)[2][RT], auto masked_tag) {
+                constexpr bool kMasked = decltype(masked_tag)::value;
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) m_ref[rt] = fmaxf(m_ref[rt], row_max(b, sacc, rt, kMasked));
+            },
+            [](const float4v (&)[2][RT]) {});
+        __syncthreads();
+        clear();
+        run_pass(accumulate, [](const float4v (&)[2][RT]) {});
     }
 
     // Normalise and store: O^T tile j element i of lane (n, qd) is dim 16*j + 4*qd + i of the
