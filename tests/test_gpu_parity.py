@@ -322,11 +322,14 @@ def test_slot_permutation_permutes_the_output_bitwise():
 
 _LAYOUT_CASES = [
     # (q_len, Hq, Hkv, format, D): one row tile at q1 (the D128 FP16 decode shape) and q2, two
-    # row tiles at q3 (one slot alone: two row groups of one tile each)
+    # row tiles at q3 (one slot alone: two row groups of one tile each), three at q8 (one slot
+    # alone: three row groups sharing one LDS ring per token half; odd tile counts at 131 and
+    # 3297 tokens, a single tile at 1 and 8)
     (1, 32, 8, "fp16", 128),
     (2, 24, 4, "e5m2", 256),
     (3, 24, 4, "e4m3", 256),
     (3, 24, 4, "fp16", 256),
+    (8, 24, 4, "e4m3", 256),
 ]
 
 
