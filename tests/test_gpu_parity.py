@@ -480,8 +480,8 @@ def test_repeatable_bitwise():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-# One encoding of 1.0 per cache format, for the spiked keys below.
-_ONE = {"e4m3": 0x38, "e5m2": 0x3C, "fp16": 1.0}
+# One encoding of 1.5 per cache format, for the spiked keys below.
+_SPIKE = {"e4m3": 0x3C, "e5m2": 0x3E, "fp16": 1.5}
 # (kv_format, head_dim) of the five kernels, and q_len at six query heads per KV head giving one,
 # two and three row tiles (12, 24 and 48 packed rows).
 _FORMATS = [("e4m3", 256), ("e5m2", 256), ("fp16", 256), ("fp16", 128), ("e4m3", 128)]
@@ -506,11 +506,11 @@ def _spike_keys(c, spikes, value):
 @pytest.mark.parametrize("fmt,head_dim", _FORMATS, ids=[f"{f}-d{d}" for f, d in _FORMATS])
 @pytest.mark.parametrize("batch", [1, 8])
 def test_reference_slack_overflow_recompute(batch, fmt, head_dim, row_tiles):
-    # Q = 1 everywhere; K is 0 except spikes of 1.0 in every dim, which score sqrt(D) (16 or 11.3,
-    # i.e. 23 or 16 log2 units) above the zero keys. The first 64 tokens of every 512-token split
-    # are zero, so each wave's first tile sets a reference of 0 and a later spike exceeds it by
-    # more than the 2^10 slack: every split is recomputed with its exact row maxima. This runs
-    # the recompute in every kernel (format x row tiles); at B8 (lengths under 1024 tokens and a
+    # Q = 1 everywhere; K is 0 except spikes of 1.5 in every dim, which score 1.5 sqrt(D) (24 or 17,
+    # i.e. 35 or 24 log2 units) above the zero keys. The first 64 tokens of every 512-token split
+    # are zero, so each wave's first tile sets a reference of 0 and a later spike's P (2^35 or
+    # 2^24) overflows FP16: every split is recomputed with its exact row maxima. This runs the
+    # recompute in every kernel (format x row tiles); at B8 (lengths under 1024 tokens and a
     # 65536-token plan) the workgroups hold two KV heads (four for E4M3 at D128).
     q_len = _ROW_TILES[row_tiles]
     lens = [900, 700, 1000, 513, 64, 899, 640, 1023][:batch]
@@ -520,7 +520,7 @@ def test_reference_slack_overflow_recompute(batch, fmt, head_dim, row_tiles):
               max_seq_len=65536 if batch > 1 else None)
     c["q"].fill_(1.0)
     spikes = [[j for j in range(L) if j % 97 == 0 and j % 512 >= 64] for L in lens]
-    _spike_keys(c, spikes, _ONE[fmt])
+    _spike_keys(c, spikes, _SPIKE[fmt])
     plan = plan_for(c)
     if batch > 1:
         gs, cus = plan.info["grid_splits"], plan.info["num_cus"]
@@ -541,10 +541,10 @@ def test_row_group_workgroups_recompute_like_batched_bitwise(fmt, head_dim, q_le
     # at q8, tile 1 of 24 rows at q4) or, for the one-byte formats at D256 and 48 rows, three (one
     # row tile per wave pair); B8 of the same 65536-token plan runs one group. Spiked keys past the
     # first 64 tokens of every 512-token split score only the rows of the 16-row tile starting at
-    # `hot_tile` (Q = 1) more than the slack above their reference; the other rows (Q scaled by
-    # 0.05) stay within it, but their bits still depend on whether their wave recomputes. Both
-    # layouts must recompute the same rows: each slot alone gives the batched bits, and both match
-    # the oracle.
+    # `hot_tile` (Q = 1) so far above their reference that P overflows FP16; the other rows (Q
+    # scaled by 0.05) stay near it, but their bits still depend on whether their wave recomputes.
+    # Both layouts must recompute the same rows: each slot alone gives the batched bits, and both
+    # match the oracle.
     lens = [900, 700, 1000, 513, 64, 899, 640, 1023]
     note(f"row groups vs one group under a partial recompute, {fmt} D{head_dim} q{q_len}")
     c = _case(batch=8, seq_lens=lens, q_len=q_len, num_q_heads=24, num_kv_heads=4, head_dim=head_dim,
@@ -561,7 +561,7 @@ def test_row_group_workgroups_recompute_like_batched_bitwise(fmt, head_dim, q_le
         j = torch.tensor([t for t in range(L) if t % 97 == 0 and t % 512 >= 64], dtype=torch.long, device="cuda")
         if len(j):
             pages = c["block_table"][b].long()[j // ps]
-            kc[pages, j % ps] = _ONE[fmt]
+            kc[pages, j % ps] = _SPIKE[fmt]
     plan = plan_for(c)
     gs, cus = plan.info["grid_splits"], plan.info["num_cus"]
     assert 8 * 4 * gs > cus >= 4 * gs          # batched: one group; one slot: row groups
@@ -573,13 +573,17 @@ def test_row_group_workgroups_recompute_like_batched_bitwise(fmt, head_dim, q_le
         assert torch.equal(single[0].view(torch.int16), batched[b].view(torch.int16)), b
 
 
-def test_reference_slack_mild_rise_single_pass():
-    # A rise of 8.7 log2 units (< the slack) after the first tiles takes the single-pass path.
-    note("reference mild rise, single pass")
+@pytest.mark.parametrize("spike,rise", [(0x2C, 8.7), (0x31, 13.0), (0x32, 14.4)])
+def test_reference_rise_below_fp16_overflow_single_pass(spike, rise):
+    # Later keys score 8.7, 13.0 or 14.4 log2 units above the reference the first tiles set (E4M3
+    # 0.375, 0.5625, 0.625 in every dim against zero keys: 256 k / 16 * log2(e)): P reaches up to
+    # 2^14.4, still finite in FP16, so the split takes one pass with those large weights and must
+    # match the oracle.
+    note(f"reference rise of {rise} log2 units, single pass")
     c = _case(batch=1, seq_lens=[900], q_len=8, num_q_heads=6, num_kv_heads=1, head_dim=256, page_size=16,
               seed=14)
     c["q"].fill_(1.0)
-    _spike_keys(c, [[j for j in range(900) if j % 97 == 0 and j >= 64]], 0x2C)      # 0.375 -> score 6
+    _spike_keys(c, [[j for j in range(900) if j % 97 == 0 and j >= 64]], spike)
     compare(run_gpu(c), run_oracle(c))
 
 

@@ -26,9 +26,10 @@
 //    second MFMA straight from registers; each lane loads 16 contiguous V bytes per token and
 //    a byte permute regroups them per dim.
 //  * Row ownership is identical in both products (row = lane % 16), so the softmax statistics
-//    stay lane-local; the max is reduced across the 4 lanes of a row. Exponentials use a fixed
-//    per-row reference (with a recompute pass if a later tile exceeds it by too much), so the
-//    O accumulators are never rescaled.
+//    stay lane-local; the max of a wave's first tile is reduced across the 4 lanes of a row and
+//    becomes the row's fixed reference for the split (with a recompute pass if a later score
+//    exceeds it by so much that P overflows FP16), so the O accumulators are never rescaled and
+//    later tiles take no maximum at all.
 //  * E4M3 / E5M2 -> FP16 are exact (every finite value of either is an FP16 value); k_scale is
 //    folded into the FP32 score scale and v_scale is applied once in the combine.
 //  * Each split writes an FP32 panel {O[rows][D], m[rows], l[rows]} (m in log2 units of the
@@ -83,7 +84,6 @@ __device__ __forceinline__ int32_t clamp_len(int32_t L, int32_t max_len) {
     return L < 0 ? 0 : (L > max_len ? max_len : L);
 }
 
-constexpr float kRefSlack = 10.0f;
 // Block-table entries one split can touch: partitions are at most 32768 tokens and pages hold
 // at least 16 tokens, so a split spans at most 32768/16 + 1 pages.
 constexpr int kMaxSplitPages = 32768 / 16 + 2;
@@ -568,15 +568,15 @@ __device__ __forceinline__ void vm_wait_tile_v() {
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Softmax step of one tile: masked raw scores (lane holds row n's tokens j0 + 16*tt + 4*qd + i of
-// the NG granules of scores), exponentials exp2(c*x - m) against the row references (c > 0,
-// log2 units), P^T in FP16. Returns true (uniformly) when a row's tile max exceeds its reference
-// by more than kRefSlack; the references are then raised and nothing was accumulated. The row
-// sums of P are taken by row_sums, from the FP16 P that the PV product uses.
-template <int RT, int NG, int TILE, class PopT>
-__device__ __forceinline__ bool softmax_tile(const float4v (&sacc)[2][RT], int32_t j0, int32_t mask_from,
-                                             const int32_t (&lim)[RT], float c, float (&m_ref)[RT],
-                                             PopT (&pop)[RT], int qd) {
+// Softmax step against fixed references, without a row maximum after the first tile. Every row
+// that sees a key in a wave's tiles sees the first of them (a row's visible keys are a prefix),
+// so that tile sets each row's reference (FIRST; a row without a key keeps -inf and only meets
+// masked scores). Later tiles take exp2(c*x - m) directly; a score far above its reference
+// makes P overflow FP16, which the row sums of the pass then show as non-finite.
+template <int RT, int NG, int TILE, bool FIRST, class PopT>
+__device__ __forceinline__ void softmax_fixed(const float4v (&sacc)[2][RT], int32_t j0, int32_t mask_from,
+                                              const int32_t (&lim)[RT], float c, float (&m_ref)[RT],
+                                              PopT (&pop)[RT], int qd) {
     constexpr int NV = 4 * NG;
     float x[RT][NV];
 #pragma unroll
@@ -594,31 +594,31 @@ __device__ __forceinline__ bool softmax_tile(const float4v (&sacc)[2][RT], int32
                 for (int i = 0; i < 4; ++i)
                     x[rt][tt * 4 + i] = (j0 + 16 * tt + 4 * qd + i) < lim[rt] ? x[rt][tt * 4 + i] : -INFINITY;
     }
-    float mx[RT];
-    bool over = false;
+    if constexpr (FIRST) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        float m = NG == 2 ? max3f(max3f(x[rt][0], x[rt][1], x[rt][2]), max3f(x[rt][3], x[rt][4 % NV], x[rt][5 % NV]),
-                                  max3f(x[rt][6 % NV], x[rt][7 % NV], x[rt][7 % NV]))
-                          : max3f(max3f(x[rt][0], x[rt][1], x[rt][2]), x[rt][3], x[rt][3]);
-        m = quad_max(m);
-        m *= c;                                      // c > 0: max commutes with the scale
-        mx[rt] = m;
-        over |= m > m_ref[rt] + kRefSlack && m_ref[rt] != -INFINITY;
-    }
-    if (__any(over)) {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) m_ref[rt] = fmaxf(m_ref[rt], mx[rt]);
-        return true;
+        for (int rt = 0; rt < RT; ++rt) {
+            float m = NG == 2 ? max3f(max3f(x[rt][0], x[rt][1], x[rt][2]), max3f(x[rt][3], x[rt][4 % NV], x[rt][5 % NV]),
+                                      max3f(x[rt][6 % NV], x[rt][7 % NV], x[rt][7 % NV]))
+                              : max3f(max3f(x[rt][0], x[rt][1], x[rt][2]), x[rt][3], x[rt][3]);
+            m = quad_max(m) * c;
+            if (m_ref[rt] == -INFINITY) m_ref[rt] = m;
+        }
     }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        if (m_ref[rt] == -INFINITY) m_ref[rt] = mx[rt];        // first tile with a visible key
         const float neg_m = m_ref[rt] == -INFINITY ? 0.0f : -m_ref[rt];
 #pragma unroll
         for (int e = 0; e < NV; ++e) pop[rt][e] = (_Float16)fast_exp2(__builtin_fmaf(x[rt][e], c, neg_m));
     }
-    return false;
+}
+
+// True in every lane when some row sum of this wave is not finite (a P overflowed FP16).
+template <int RT>
+__device__ __forceinline__ bool sums_overflowed(const float4v (&lsum)[RT]) {
+    bool bad = false;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) bad |= !(lsum[rt][0] <= 3.4028235e38f);
+    return __any(bad);
 }
 
 // Row sums of a tile's P on the matrix cores: a 16 x K block of ones times P^T (K tokens x 16 rows)
@@ -845,13 +845,16 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP * RG, split_waves_per_simd<
     constexpr int32_t kStride = kWavesPerHead * F::TILE;        // tokens between a wave's tiles
     const int32_t first = j_begin + half * F::TILE;              // this wave's first tile
 
-    // Per-row reference max (log2 units). A row's reference is the max of the first tile in
-    // which the wave sees a key for it; exponentials are taken against it, so O and l never
-    // need rescaling and the O accumulators are touched only by MFMAs. A later tile may exceed
-    // the reference by up to kRefSlack (P <= 2^kRefSlack, exact range in FP16 and FP32). If one
-    // exceeds it by more, the wave (with row groups: both waves of its token half) recomputes its
-    // tiles once with each row's exact maximum over the split as its reference (then no tile can
-    // exceed it). Both passes depend only on the split's own data, so the result is deterministic.
+    // Per-row reference max (log2 units). A row's reference is the max of the wave's first tile
+    // (a row's visible keys are a prefix, so a row that sees any key of the wave's tiles sees one
+    // in the first); exponentials are taken against it, so O and l never need rescaling and the
+    // O accumulators are touched only by MFMAs. A later score may exceed the reference by almost
+    // 16 log2 units: P then stays a finite FP16 value with FP16's full relative precision, and
+    // the FP32 sums of P and P*V stay far from overflow. A score higher still makes its P infinite
+    // in FP16, which the row sums show at the end of the pass; the wave (with row groups: every
+    // wave of its token half) then recomputes its tiles once with each row's exact maximum over
+    // the split as its reference (then no P exceeds 1). Both passes depend only on the split's
+    // own data, so the result is deterministic.
     float m_ref[RT];
     float4v lsum[RT];        // row sums of P: every element of lane (n, qd) holds packed row n's
     float4v o[RT][JT];
@@ -870,12 +873,12 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP * RG, split_waves_per_simd<
             issue_k<F, RG == 1>(gk, last, lo, ring0 + k * G::STAGE, p, lane);
             issue_v<F, RG == 1>(gk, last, lo, ring0 + k * G::STAGE, p, n, qd, lane);
         }
-        bool over = false;
         int32_t j0 = first;
+        int st = 0;
         // Granules of the tile that refills the current stage; the next one is looked up during
         // the current tile's MFMAs, so its block-table read does not stall the loop head.
         Granules gn = granules<F>(first + G::NS * kStride, last, pages, pg0, kbase, vbase, p);
-        for (int st = 0;; st = (st + 1) % G::NS) {
+        auto tile = [&](auto first_tag) {
             const uint32_t stage = ring0 + st * G::STAGE;
             const uint8_t* stage_bytes = ring + st * G::STAGE;
             vm_wait_tile_k<F>();                // tile k's K has landed
@@ -902,7 +905,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP * RG, split_waves_per_simd<
                 gn = granules<F>(j0 + (G::NS + 1) * kStride, last, pages, pg0, kbase, vbase, p);
             }
             typename F::PopT pop[RT];
-            over = softmax_tile<RT, F::NG, F::TILE>(sacc, j0, mask_from, lim, c, m_ref, pop, qd);
+            softmax_fixed<RT, F::NG, F::TILE, decltype(first_tag)::value>(sacc, j0, mask_from, lim, c, m_ref, pop, qd);
             if constexpr (F::ROW == 128) {
                 vm_wait_tile_v<F>();
                 tv = read_v<F>(stage_bytes, n, qd, lane);
@@ -910,12 +913,14 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP * RG, split_waves_per_simd<
                 issue_v<F, RG == 1>(gn, last, lo, stage, p, n, qd, lane);
                 gn = granules<F>(j0 + (G::NS + 1) * kStride, last, pages, pg0, kbase, vbase, p);
             }
-            if (over) break;
             F::template pv<RT>(tv, pop, o);
             row_sums<RT>(pop, lsum);
             j0 += kStride;
-            if (j0 > last) break;
-        }
+            st = (st + 1) % G::NS;
+        };
+        tile(std::true_type{});
+        while (j0 <= last) tile(std::false_type{});
+        const bool over = sums_overflowed<RT>(lsum);
         vm_wait_all();   // no load may still be writing the ring when the wave moves on
         return over;
     };
@@ -1014,46 +1019,6 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP * RG, split_waves_per_simd<
     }
 }
 
-// The softmax step without the exit (for loops that every wave of a workgroup must run to the
-// same end): a row whose tile max exceeds its reference by more than the slack sets `over` (per
-// lane) and P is computed against the unchanged references - that pass's result is discarded
-// and recomputed. Without an overflow it computes exactly what softmax_tile computes.
-template <int RT, int NG, int TILE, class PopT>
-__device__ __forceinline__ void softmax_tile_nx(const float4v (&sacc)[2][RT], int32_t j0, int32_t mask_from,
-                                                const int32_t (&lim)[RT], float c, float (&m_ref)[RT],
-                                                PopT (&pop)[RT], int qd, bool& over) {
-    constexpr int NV = 4 * NG;
-    float x[RT][NV];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int tt = 0; tt < NG; ++tt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[rt][tt * 4 + i] = sacc[tt][rt][i];
-    if (j0 + TILE > mask_from) {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int tt = 0; tt < NG; ++tt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    x[rt][tt * 4 + i] = (j0 + 16 * tt + 4 * qd + i) < lim[rt] ? x[rt][tt * 4 + i] : -INFINITY;
-    }
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        float m = NG == 2 ? max3f(max3f(x[rt][0], x[rt][1], x[rt][2]), max3f(x[rt][3], x[rt][4 % NV], x[rt][5 % NV]),
-                                  max3f(x[rt][6 % NV], x[rt][7 % NV], x[rt][7 % NV]))
-                          : max3f(max3f(x[rt][0], x[rt][1], x[rt][2]), x[rt][3], x[rt][3]);
-        m = quad_max(m);
-        m *= c;
-        over |= m > m_ref[rt] + kRefSlack && m_ref[rt] != -INFINITY;
-        if (m_ref[rt] == -INFINITY) m_ref[rt] = m;
-        const float neg_m = m_ref[rt] == -INFINITY ? 0.0f : -m_ref[rt];
-#pragma unroll
-        for (int e = 0; e < NV; ++e) pop[rt][e] = (_Float16)fast_exp2(__builtin_fmaf(x[rt][e], c, neg_m));
-    }
-}
-
 // Three row groups (one-byte formats at D = 256, 33 to 48 packed rows, grids of at most one
 // workgroup per CU): six waves per (slot, KV head, split), wave w taking row tile w / 2 over the
 // tiles of token half w % 2. The three waves of a half share one three-stage LDS ring: the
@@ -1062,10 +1027,10 @@ __device__ __forceinline__ void softmax_tile_nx(const float4v (&sacc)[2][RT], in
 // tile both publishes tile k (the loader has waited for its own loads) and frees the stage of
 // tile k-1 (every wave has read it), which then takes tile k+2. Per wave this is a third of the rows' MFMA
 // and softmax work of the one-group kernel, and six waves keep every SIMD busy. Every wave runs
-// the same number of iterations (the shorter half idles through its last one) and the loop has
-// no exit; a half recomputes with exact row maxima when any of its three waves saw a tile exceed
-// a reference by more than the slack - the rows and tiles whose overflow decides the recompute of
-// the one-group wave of that half - so the result has the same bits as the other layouts.
+// the same number of iterations (the shorter half idles through its last one); a half recomputes
+// with exact row maxima when a row sum of any of its three waves is not finite - the rows and
+// tiles whose overflow decides the recompute of the one-group wave of that half - so the result
+// has the same bits as the other layouts.
 constexpr int kRg3Waves = 6;
 constexpr int kRg3Stages = 3;
 
@@ -1187,7 +1152,6 @@ __global__ __launch_bounds__(64 * kRg3Waves) void split_kernel_rg3(RunParams p) 
     // One pass over the split; every wave runs `iters` iterations with one barrier each. With
     // `compute` false the wave only keeps the ring going (its half needs no recompute).
     auto run_pass = [&](bool compute) -> bool {
-        bool over = false;
         if (compute) {
             lsum[0] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1213,7 +1177,8 @@ __global__ __launch_bounds__(64 * kRg3Waves) void split_kernel_rg3(RunParams p) 
                 F::template qk<1>(tk, sacc, qop);
                 const TileV tv = read_v<F>(stage_bytes, n, qd, lane);
                 typename F::PopT pop[1];
-                softmax_tile_nx<1, F::NG, F::TILE>(sacc, j0, mask_from, lim, c, m_ref, pop, qd, over);
+                if (it == 0) softmax_fixed<1, F::NG, F::TILE, true>(sacc, j0, mask_from, lim, c, m_ref, pop, qd);
+                else softmax_fixed<1, F::NG, F::TILE, false>(sacc, j0, mask_from, lim, c, m_ref, pop, qd);
                 F::template pv<1>(tv, pop, o);
                 row_sums<1>(pop, lsum);
                 lds_wait_all();                // this tile's reads are done before the next barrier
@@ -1221,7 +1186,7 @@ __global__ __launch_bounds__(64 * kRg3Waves) void split_kernel_rg3(RunParams p) 
             j0 += kStride;
         }
         vm_wait_all();
-        return __any(over);
+        return compute && sums_overflowed<1>(lsum);
     };
 
     m_ref[0] = -INFINITY;
