@@ -1021,18 +1021,19 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP * RG, split_waves_per_simd<
 
 // Three row groups (one-byte formats at D = 256, 33 to 48 packed rows, grids of at most one
 // workgroup per CU): six waves per (slot, KV head, split), wave w taking row tile w / 2 over the
-// tiles of token half w % 2. The three waves of a half share one three-stage LDS ring: the
+// tiles of token half w % 2. The three waves of a half share one four-stage LDS ring: the
 // second of them (row tile 1; waves 2 and 3, the two waves alone on their SIMDs - waves 4 and 5
 // share SIMDs with waves 0 and 1) issues the K and V loads of each tile, and one barrier per
 // tile both publishes tile k (the loader has waited for its own loads) and frees the stage of
-// tile k-1 (every wave has read it), which then takes tile k+2. Per wave this is a third of the rows' MFMA
-// and softmax work of the one-group kernel, and six waves keep every SIMD busy. Every wave runs
+// tile k-1 (every wave has read it), which then takes tile k+3, so three tiles per half are in
+// flight. Per wave this is a third of the rows' MFMA and softmax work of the one-group kernel,
+// and six waves keep every SIMD busy. Every wave runs
 // the same number of iterations (the shorter half idles through its last one); a half recomputes
 // with exact row maxima when a row sum of any of its three waves is not finite - the rows and
 // tiles whose overflow decides the recompute of the one-group wave of that half - so the result
 // has the same bits as the other layouts.
 constexpr int kRg3Waves = 6;
-constexpr int kRg3Stages = 3;
+constexpr int kRg3Stages = 4;
 
 template <int FMT>
 __global__ __launch_bounds__(64 * kRg3Waves) void split_kernel_rg3(RunParams p) {
@@ -1159,12 +1160,13 @@ __global__ __launch_bounds__(64 * kRg3Waves) void split_kernel_rg3(RunParams p) 
         }
         load_tile(0, 0);
         load_tile(1, 1);
+        load_tile(2, 2);
         int32_t j0 = first;
         for (int it = 0; it < iters; ++it) {
-            // The loader's loads of tile `it` have landed (tile it+1's may still be in flight).
-            if (rg == 1) vm_wait_n<G::KLOADS + G::VLOADS>();
+            // The loader's loads of tile `it` have landed (tiles it+1 and it+2 may still be in flight).
+            if (rg == 1) vm_wait_n<2 * (G::KLOADS + G::VLOADS)>();
             __syncthreads();                   // tile it in LDS for all; tile it-1 read by all
-            load_tile(it + 2, (it + 2) % kRg3Stages);
+            load_tile(it + 3, (it + 3) % kRg3Stages);
             if (compute && j0 <= last) {
                 const uint8_t* stage_bytes = ring + (it % kRg3Stages) * G::STAGE;
                 TileK tk;
