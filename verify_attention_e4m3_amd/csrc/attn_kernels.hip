@@ -621,6 +621,86 @@ __device__ __forceinline__ bool sums_overflowed(const float4v (&lsum)[RT]) {
     return __any(bad);
 }
 
+// The slot a workgroup's grid position `b` serves and its clamped length. With order_by_work
+// (batches of 2 to 64 slots) the positions go to the slots in order of decreasing partition
+// length (then slot index), so the longest-running workgroups are dispatched first and the short
+// ones fill in behind them; otherwise position b is slot b. Which workgroup serves a (slot,
+// split) changes nothing in its arithmetic. Every lane reads one slot's length; `b` is updated
+// in place to the slot index (wave-uniform).
+__device__ __forceinline__ int32_t slot_for_position(const RunParams& p, int lane, int& b) {
+    if (!p.order_by_work) return clamp_len(p.seq_lens[b], p.max_seq_len);
+    const int32_t Ll = lane < p.batch ? clamp_len(p.seq_lens[lane], p.max_seq_len) : 0;
+    const int32_t wk = lane < p.batch ? (Ll > 0 ? partition_len(Ll, p.policy) : 0) : -1;
+    int rank = 0;
+    for (int k = 0; k < p.batch; ++k) {
+        const int32_t wkk = __builtin_amdgcn_readlane(wk, k);
+        rank += (wkk > wk) | ((wkk == wk) & (k < lane));
+    }
+    const uint64_t hit = __ballot(lane < p.batch && rank == b);   // exactly one lane: ranks are a permutation
+    if (hit != 0) b = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+    return __builtin_amdgcn_readlane(Ll, b);
+}
+
+// Q^T operands of row tiles rt0 .. rt0+RT-1 of KV head g of slot b, kept in registers for the
+// whole split: entry (rt, ks) holds the 8 dims of k-step ks (F::q_dim) of packed row
+// (rt0 + rt)*16 + n (zeros past q_len*G) - the dim order of the K operand, so the contraction
+// pairs matching dims. lim[rt]: keys j < lim are visible to the row (the verify token t sits at
+// position L - q_len + t), capped at the split's end.
+template <class F, int RT>
+__device__ __forceinline__ void load_q_rows(const RunParams& p, int b, int g, int rt0, int n, int qd, int32_t L,
+                                            int32_t j_end, half8 (&qop)[RT][F::KSTEPS], int32_t (&lim)[RT]) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int r = (rt0 + rt) * 16 + n;
+        const int t = r / p.group;
+        const int h = g * p.group + (r - t * p.group);
+        const bool live = r < p.rows;
+        const uint16_t* qrow = p.q + (((int64_t)b * p.q_len + (live ? t : 0)) * p.num_q_heads + (live ? h : 0)) * F::D;
+#pragma unroll
+        for (int ks = 0; ks < F::KSTEPS; ++ks) {
+            const half8 v = *reinterpret_cast<const half8*>(qrow + F::q_dim(ks, qd));
+            qop[rt][ks] = live ? v : half8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+        const int32_t lr = p.causal ? (L - p.q_len + 1 + t) : L;
+        lim[rt] = min(lr, j_end);
+    }
+}
+
+// Stages the block-table entries of the pages that tokens j_begin .. last of slot b touch,
+// clamped into the caches, in LDS (`NT` threads share the copy; the caller's barrier publishes
+// it), so the tile loops issue no compiler-visible global load, whose wait would also drain the
+// ring. Returns the index of the split's first page.
+template <int NT>
+__device__ __forceinline__ int32_t stage_pages(const RunParams& p, int b, int32_t j_begin, int32_t last,
+                                               int32_t* pages) {
+    int32_t pg0, pg_last, unused_slot;
+    locate(j_begin, p, pg0, unused_slot);
+    locate(last, p, pg_last, unused_slot);
+    const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
+    for (int i = threadIdx.x; i <= pg_last - pg0; i += NT) {
+        const int32_t v = bt[pg0 + i];
+        pages[i] = v < 0 ? 0 : (v >= p.num_pages ? (int32_t)(p.num_pages - 1) : v);
+    }
+    return pg0;
+}
+
+// Score scale in log2 units, c = sm_scale * k_scale * log2(e). The softmax takes the max of the
+// raw scores and scales it, which needs c > 0: a negative k_scale is moved into Q (negating FP16
+// is exact) and c = 0 is raised to the smallest normal float, which leaves every exp2 argument
+// unchanged (|score| * 2^-126 rounds away) but keeps -inf * c = -inf.
+template <int RT, int KS>
+__device__ __forceinline__ float score_scale(const RunParams& p, half8 (&qop)[RT][KS]) {
+    float c = p.sm_scale * (*p.k_scale) * kLog2e;
+    if (c < 0.0f) {
+        c = -c;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qop[rt][ks] = -qop[rt][ks];
+    }
+    return fmaxf(c, 1.17549435e-38f);
+}
+
 // Row sums of a tile's P on the matrix cores: a 16 x K block of ones times P^T (K tokens x 16 rows)
 // adds, in every element of lane (n, qd)'s accumulator, the sum of packed row n's K weights - one
 // MFMA per row tile instead of a VALU add tree, over the same FP16 weights the PV product uses.
@@ -739,25 +819,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP * RG, split_waves_per_simd<
     wg /= head_groups;
     const int s = wg % p.grid_splits;
     int b = wg / p.grid_splits;
-    int32_t L;
-    if (p.order_by_work) {
-        // Slot positions in the grid go to the slots in order of decreasing partition length
-        // (then slot index), so the longest-running workgroups are dispatched first and the short
-        // ones fill in behind them. Which workgroup serves a (slot, split) changes nothing in
-        // its arithmetic.
-        const int32_t Ll = lane < p.batch ? clamp_len(p.seq_lens[lane], p.max_seq_len) : 0;
-        const int32_t wk = lane < p.batch ? (Ll > 0 ? partition_len(Ll, p.policy) : 0) : -1;
-        int rank = 0;
-        for (int k = 0; k < p.batch; ++k) {
-            const int32_t wkk = __builtin_amdgcn_readlane(wk, k);
-            rank += (wkk > wk) | ((wkk == wk) & (k < lane));
-        }
-        const uint64_t hit = __ballot(lane < p.batch && rank == b);   // exactly one lane: ranks are a permutation
-        if (hit != 0) b = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
-        L = __builtin_amdgcn_readlane(Ll, b);
-    } else {
-        L = clamp_len(p.seq_lens[b], p.max_seq_len);
-    }
+    const int32_t L = slot_for_position(p, lane, b);
     const int32_t S = num_splits(L, p.policy);
     if (s >= S) return;                 // uniform over the workgroup
     const int32_t P = partition_len(L, p.policy);
@@ -765,40 +827,11 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP * RG, split_waves_per_simd<
     const int32_t j_end = min(j_begin + P, L);
     const int32_t last = j_end - 1;
 
-    // Q^T operands stay in registers for the whole split: entry (rt, ks) holds the 8 dims of
-    // k-step ks (F::q_dim) of packed row (rt0 + rt)*16 + n (zeros past q_len*G) - the dim order of
-    // the K operand, so the contraction pairs matching dims.
+    // Q^T operands and visibility limits of the wave's row tiles.
     half8 qop[RT][KS];
     int32_t lim[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const int r = (rt0 + rt) * 16 + n;
-        const int t = r / p.group;
-        const int h = g * p.group + (r - t * p.group);
-        const bool live = r < p.rows;
-        const uint16_t* qrow = p.q + (((int64_t)b * p.q_len + (live ? t : 0)) * p.num_q_heads + (live ? h : 0)) * D;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const half8 v = *reinterpret_cast<const half8*>(qrow + F::q_dim(ks, qd));
-            qop[rt][ks] = live ? v : half8{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-        // Keys j < lim are visible to this row: the verify token t sits at position L - q_len + t.
-        const int32_t lr = p.causal ? (L - p.q_len + 1 + t) : L;
-        lim[rt] = min(lr, j_end);
-    }
-    // Score scale in log2 units, c = sm_scale * k_scale * log2(e). The softmax takes the max of
-    // the raw scores and scales it, which needs c > 0: a negative k_scale is moved into Q
-    // (negating FP16 is exact) and c = 0 is raised to the smallest normal float, which leaves
-    // every exp2 argument unchanged (|score| * 2^-126 rounds away) but keeps -inf * c = -inf.
-    float c = p.sm_scale * (*p.k_scale) * kLog2e;
-    if (c < 0.0f) {
-        c = -c;
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) qop[rt][ks] = -qop[rt][ks];
-    }
-    c = fmaxf(c, 1.17549435e-38f);
+    load_q_rows<F, RT>(p, b, g, rt0, n, qd, L, j_end, qop, lim);
+    const float c = score_scale(p, qop);
     // Make the Q loads land before the ring is primed: otherwise the compiler's waits for them,
     // placed at their first use, would count the ring loads issued in between and wait for those.
 #pragma unroll
@@ -814,16 +847,7 @@ __global__ __launch_bounds__(64 * kWavesPerHead * HP * RG, split_waves_per_simd<
     // compiler-visible global load (whose wait would also drain the ring).
     __shared__ SplitLds<NW, Geo<F>::RING> lds;
     int32_t* pages = lds.pages;
-    int32_t pg0, pg_last, unused_slot;
-    locate(j_begin, p, pg0, unused_slot);
-    locate(last, p, pg_last, unused_slot);
-    {
-        const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
-        for (int i = threadIdx.x; i <= pg_last - pg0; i += 64 * NW) {
-            const int32_t v = bt[pg0 + i];
-            pages[i] = v < 0 ? 0 : (v >= p.num_pages ? (int32_t)(p.num_pages - 1) : v);
-        }
-    }
+    const int32_t pg0 = stage_pages<64 * NW>(p, b, j_begin, last, pages);
     __syncthreads();
 
     // Per-wave LDS ring of NS stages: the wave's k-th tile lives in stage k % NS. Its tiles
@@ -1056,21 +1080,7 @@ __global__ __launch_bounds__(64 * kRg3Waves) void split_kernel_rg3(RunParams p) 
     wg /= p.num_kv_heads;
     const int s = wg % p.grid_splits;
     int b = wg / p.grid_splits;
-    int32_t L;
-    if (p.order_by_work) {
-        const int32_t Ll = lane < p.batch ? clamp_len(p.seq_lens[lane], p.max_seq_len) : 0;
-        const int32_t wk = lane < p.batch ? (Ll > 0 ? partition_len(Ll, p.policy) : 0) : -1;
-        int rank = 0;
-        for (int k = 0; k < p.batch; ++k) {
-            const int32_t wkk = __builtin_amdgcn_readlane(wk, k);
-            rank += (wkk > wk) | ((wkk == wk) & (k < lane));
-        }
-        const uint64_t hit = __ballot(lane < p.batch && rank == b);
-        if (hit != 0) b = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
-        L = __builtin_amdgcn_readlane(Ll, b);
-    } else {
-        L = clamp_len(p.seq_lens[b], p.max_seq_len);
-    }
+    const int32_t L = slot_for_position(p, lane, b);
     const int32_t S = num_splits(L, p.policy);
     if (s >= S) return;                 // uniform over the workgroup
     const int32_t P = partition_len(L, p.policy);
@@ -1078,30 +1088,11 @@ __global__ __launch_bounds__(64 * kRg3Waves) void split_kernel_rg3(RunParams p) 
     const int32_t j_end = min(j_begin + P, L);
     const int32_t last = j_end - 1;
 
-    // Q^T operands and visibility limit of this wave's row tile (as in split_kernel).
+    // Q^T operands and visibility limit of this wave's row tile.
     half8 qop[1][KS];
     int32_t lim[1];
-    {
-        const int r = rg * 16 + n;
-        const int t = r / p.group;
-        const int h = g * p.group + (r - t * p.group);
-        const bool live = r < p.rows;
-        const uint16_t* qrow = p.q + (((int64_t)b * p.q_len + (live ? t : 0)) * p.num_q_heads + (live ? h : 0)) * D;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const half8 v = *reinterpret_cast<const half8*>(qrow + F::q_dim(ks, qd));
-            qop[0][ks] = live ? v : half8{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-        const int32_t lr = p.causal ? (L - p.q_len + 1 + t) : L;
-        lim[0] = min(lr, j_end);
-    }
-    float c = p.sm_scale * (*p.k_scale) * kLog2e;
-    if (c < 0.0f) {
-        c = -c;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qop[0][ks] = -qop[0][ks];
-    }
-    c = fmaxf(c, 1.17549435e-38f);
+    load_q_rows<F, 1>(p, b, g, rg, n, qd, L, j_end, qop, lim);
+    const float c = score_scale(p, qop);
 #pragma unroll
     for (int ks = 0; ks < KS; ks += 2) asm volatile("" ::"v"(qop[0][ks]), "v"(qop[0][ks + 1]));
     const int32_t mask_from = p.causal ? min(j_end, L - p.q_len + 1) : j_end;
@@ -1115,16 +1106,7 @@ __global__ __launch_bounds__(64 * kRg3Waves) void split_kernel_rg3(RunParams p) 
     };
     __shared__ Rg3Lds lds;
     int32_t* pages = lds.pages;
-    int32_t pg0, pg_last, unused_slot;
-    locate(j_begin, p, pg0, unused_slot);
-    locate(last, p, pg_last, unused_slot);
-    {
-        const int32_t* bt = p.block_table + (int64_t)b * p.bt_stride;
-        for (int i = threadIdx.x; i <= pg_last - pg0; i += 64 * kRg3Waves) {
-            const int32_t v = bt[pg0 + i];
-            pages[i] = v < 0 ? 0 : (v >= p.num_pages ? (int32_t)(p.num_pages - 1) : v);
-        }
-    }
+    const int32_t pg0 = stage_pages<64 * kRg3Waves>(p, b, j_begin, last, pages);
     __syncthreads();
 
     uint8_t* ring = lds.rings[half];
