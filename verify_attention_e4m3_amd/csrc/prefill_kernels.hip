@@ -151,6 +151,7 @@ __device__ __forceinline__ void pf_wait_loads(int blocks) {
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+template <bool kLongestFirst>
 __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p) {
     constexpr int RT = kPfRowTilesPerWave;
     const int lane = threadIdx.x & 63;
@@ -158,9 +159,12 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
     const int n = lane & 15;         // MFMA column: query row within a row tile
     const int qd = lane >> 4;        // quarter of the wave
 
-    // Workgroup order: KV head fastest, then query tile.
+    // Workgroup order: KV head fastest, then query tile - in descending order with kLongestFirst
+    // (causal tiles see more keys the later their tokens, so the longest go first and the short
+    // ones fill in behind them when the grid takes several rounds of the CUs).
     const int g = blockIdx.x % p.num_kv_heads;
-    const int qt = blockIdx.x / p.num_kv_heads;
+    const int qi = blockIdx.x / p.num_kv_heads;
+    const int qt = kLongestFirst ? (p.q_len + p.tokens_per_wg - 1) / p.tokens_per_wg - 1 - qi : qi;
     const int32_t t0 = qt * p.tokens_per_wg;
 
     // Row tile r (0..11) of the workgroup: query tokens t0 + 16*(r / G) + 0..15 of head g*G + r%G.
@@ -424,8 +428,13 @@ attn_status attn_launch_prefill(const attn::PrefillParams& p, void* stream) {
     const unsigned q_tiles = (unsigned)((p.q_len + p.tokens_per_wg - 1) / p.tokens_per_wg);
     const unsigned grid = q_tiles * (unsigned)p.num_kv_heads;
     if (grid == 0) return ATTN_OK;
-    hipError_t e = hipLaunchKernel((const void*)attn::prefill_kernel, dim3(grid), dim3(64 * attn::kPfWaves), kargs, 0,
-                                   (hipStream_t)stream);
+    // Longest tiles first when the causal grid takes three or more rounds of the CUs (one
+    // workgroup per CU at a time); with one or two rounds the ascending order ends sooner.
+    int dev = 0, cus = 0;
+    const bool rounds3 = hipGetDevice(&dev) == hipSuccess && attn_device_cus(dev, &cus) == ATTN_OK &&
+                         grid >= 3u * (unsigned)cus;
+    const void* fn = p.causal && rounds3 ? (const void*)attn::prefill_kernel<true> : (const void*)attn::prefill_kernel<false>;
+    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(64 * attn::kPfWaves), kargs, 0, (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
