@@ -573,12 +573,13 @@ def test_row_group_workgroups_recompute_like_batched_bitwise(fmt, head_dim, q_le
         assert torch.equal(single[0].view(torch.int16), batched[b].view(torch.int16)), b
 
 
-@pytest.mark.parametrize("spike,rise", [(0x2C, 8.7), (0x31, 13.0), (0x32, 14.4)])
-def test_reference_rise_below_fp16_overflow_single_pass(spike, rise):
-    # Later keys score 8.7, 13.0 or 14.4 log2 units above the reference the first tiles set (E4M3
-    # 0.375, 0.5625, 0.625 in every dim against zero keys: 256 k / 16 * log2(e)): P reaches up to
-    # 2^14.4, still finite in FP16, so the split takes one pass with those large weights and must
-    # match the oracle.
+@pytest.mark.parametrize("spike,rise", [(0x2C, 8.7), (0x31, 13.0), (0x32, 14.4), (0x33, 15.9), (0x34, 17.3)])
+def test_reference_rise_around_fp16_overflow(spike, rise):
+    # Later keys score 8.7, 13.0, 14.4, 15.9 or 17.3 log2 units above the reference the first
+    # tiles set (E4M3 0.375, 0.5625, 0.625, 0.6875, 0.75 in every dim against zero keys: 256 k / 16
+    # * log2(e)). Up to 15.9 (P about 60000, just under the FP16 maximum) the split takes one pass
+    # with those large weights; at 17.3 P overflows FP16 and the split is recomputed with its
+    # exact row maxima. Either way the result must match the oracle.
     note(f"reference rise of {rise} log2 units, single pass")
     c = _case(batch=1, seq_lens=[900], q_len=8, num_q_heads=6, num_kv_heads=1, head_dim=256, page_size=16,
               seed=14)
