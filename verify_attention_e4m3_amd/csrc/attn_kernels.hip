@@ -781,9 +781,9 @@ __device__ __forceinline__ void split_row_max(float (&m)[RT], int32_t j_begin, i
 // of the same head and tokens (past the head's last row tile, rows without a query: zero
 // scores, never written), so each wave's tile loop carries fewer rows and every SIMD works.
 // Each row's tiles, references, products and merge are the same in both layouts, and a pair
-// recomputes with exact row maxima exactly when one of the two pairs' waves of the same token
-// half exceeded a reference - the same tokens and rows whose overflow decides the recompute of
-// a one-group wave - so the row groups never change a bit of the result.
+// recomputes with exact row maxima exactly when a row sum of either pair's wave of the same token
+// half is not finite (a P overflowed FP16) - the same tokens and rows whose overflow decides the
+// recompute of a one-group wave - so the row groups never change a bit of the result.
 constexpr int kWavesPerHead = 2;
 
 template <int NW, int RING>

@@ -270,8 +270,8 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
         return pf_quad_max(mx) * c;
     };
     // Exponentials against the fixed references, row sums, and P for the PV product. `emax`
-    // keeps the largest exponential: one above 2^slack means some score exceeded its reference
-    // by more than the slack.
+    // keeps the largest exponential: one above kPfSlackFactor (2^10) means some score exceeded
+    // its reference by more than 10 log2 units.
     float emax = 0.0f;
     auto softmax = [&](int32_t blk, const float4v (&sacc)[2][RT], half8 (&pop)[RT], auto masked_tag) {
         constexpr bool kMasked = decltype(masked_tag)::value;
